@@ -1,0 +1,188 @@
+"""Benchmark: paged varlen GQA attention with the per-token relative bias on one MI355X.
+
+A step is one ``rel_attn_fwd`` call (main attention kernel, plus the split-KV
+combine kernel when the call splits) over one batch of synthetic, seeded input
+that is resident in HBM before timing starts. Default workload: batched
+decode, 64 requests x 1 query token, KV lengths uniform in [1024, 8192],
+32 query / 8 KV heads, head_dim 128, block_size 16, rel_extent 1024, bf16.
+
+Prints ONE JSON line. ``value`` is the algorithmic bytes of a step (K/V rows
+of visible keys, in-range bias, q, out, page-table entries) divided by the
+measured step time. ``roofline`` compares the same figure (or TFLOP/s for a
+compute-bound workload) with MI355X's published peak, using per-call HIP
+event timings taken on the stream the kernels run on. ``cpu_baseline`` times
+the fp64 CPU oracle on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from paged_varlen_attention_gqa_amd import rel_attn_fwd, rel_attn_num_splits, rel_attn_workspace_bytes  # noqa: E402
+from paged_varlen_attention_gqa_amd.inputs import config_spec, make_case  # noqa: E402
+from paged_varlen_attention_gqa_amd.work import case_work  # noqa: E402
+
+METRIC = "rel-bias paged attn: decode KV GB/s + prefill TFLOP/s, % of MI355X roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+DESCRIPTIONS = {
+    "decode_b64": "batched decode: 64 requests x 1 query, KV lens U[1024,8192], H=32 Hkv=8 D=128 "
+                  "bs=16, 40000-page pool, causal, rel_extent=1024, bf16",
+    "prefill_chunked": "chunked causal prefill: 4 requests x 2048 queries over prior context "
+                       "0/1024/2048/4096, H=64 Hkv=8 D=128 bs=16, rel_extent=4096, bf16",
+    "mixed_window": "mixed sliding-window batch: 8 prefills (512 queries over KV 4096) + 56 decodes "
+                    "(KV U[2048,32768]), window (4095,0), H=32 Hkv=4 D=128 bs=16, rel_extent=2048, bf16",
+    "decode_long_b1": "batch-1 long-context decode: 1 query over 262144 keys, H=32 Hkv=4 D=128 "
+                      "bs=64, rel_extent=8192, bf16, split-KV + LSE combine",
+    "tiny_fp32": "tiny fp32 correctness case: 2 requests, query lens 5/17, KV lens 37/70, H=4 Hkv=2 "
+                 "D=64 bs=16, rel_extent=32",
+}
+BOUND = {"decode_b64": "hbm", "decode_long_b1": "hbm", "mixed_window": "hbm",
+         "prefill_chunked": "mfma", "tiny_fp32": "hbm"}
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(case, name: str, budget_s: float = 20.0) -> dict:
+    """Time the fp64 oracle on a bounded sample of the same workload (whole requests
+    for decode workloads, a token sample otherwise); scaled to GB/s or TFLOP/s."""
+    import oracle
+    from paged_varlen_attention_gqa_amd.work import count_work
+
+    cu = case.cu_seqlens_q.tolist()
+    B = case.batch_size
+    qlens, klens = case.query_lens(), case.kv_lens()
+    order = list(range(B))
+    done, t_total = [], 0.0
+    elem = case.q.element_size()
+    bound = BOUND[name]
+    for b in order:
+        toks = list(range(cu[b], cu[b + 1]))
+        if bound == "mfma":  # a bounded token sample of this request
+            toks = toks[-8:]
+        if not toks:
+            continue
+        t0 = time.perf_counter()
+        oracle.oracle_attention(**case.kwargs(), tokens=toks)
+        t_total += time.perf_counter() - t0
+        done.append((b, len(toks)))
+        if t_total > budget_s:
+            break
+    w = count_work(query_lens=[n for _, n in done], kv_lens=[klens[b] for b, _ in done],
+                   num_heads=case.num_heads, num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
+                   block_size=case.block_size, rel_extent=case.rel_extent, causal=case.causal,
+                   window_size=case.window_size, elem_bytes=elem)
+    cores = len(os.sched_getaffinity(0))
+    if bound == "mfma":
+        value, unit = w.flops / t_total / 1e12, "TFLOP/s"
+    else:
+        value, unit = w.bytes / t_total / 1e9, "GB/s"
+    ntok = sum(n for _, n in done)
+    return {"value": round(value, 6), "unit": unit, "cores": cores, "kind": "oracle",
+            "sample": f"{len(done)} of {B} requests ({ntok} query tokens, the last 8 of each request "
+                      f"for prefill), fp64 NumPy oracle, {t_total:.1f} s" if bound == "mfma" else
+                      f"{len(done)} of {B} requests ({ntok} query tokens), fp64 NumPy oracle, "
+                      f"{t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="decode_b64", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--num-splits", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this path has no "
+              f"multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(2)
+    name = args.config
+    dev = torch.device("cuda:0")
+    _log(f"[bench] generating {name}")
+    case = make_case(**config_spec(name))
+    work = case_work(case)
+    kw = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in case.kwargs().items()}
+    wl, wr = case.window_size
+    splits = args.num_splits or rel_attn_num_splits(
+        is_local=(wl >= 0 or wr >= 0), batch_size=case.batch_size, max_query_len=case.max_seqlen_q,
+        num_heads=case.num_heads, num_kv_heads=case.num_kv_heads, max_kv_len=max(case.kv_lens()))
+    out = torch.empty_like(kw["q"])
+    need = rel_attn_workspace_bytes(splits, case.num_tokens, case.num_heads, case.head_dim)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        rel_attn_fwd(**kw, num_splits=splits, out=out, workspace=ws)
+
+    _log(f"[bench] warmup {args.warmup} (num_splits={splits})")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    _log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    ms_per_step = wall * 1e3 / args.steps
+    gbs = work.bytes / (ms_per_step * 1e-3) / 1e9
+    tflops = work.flops / (ms_per_step * 1e-3) / 1e12
+    avg_call_s = float(call_ms.mean()) * 1e-3
+    bound = BOUND[name]
+    if bound == "mfma":
+        peak = BF16_MFMA_PEAK_TFLOPS if case.dtype == torch.bfloat16 else FP32_MFMA_PEAK_TFLOPS
+        ach = work.flops / avg_call_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 3), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4), "traffic": None}
+        value, unit = tflops, "TFLOP/s"
+    else:
+        ach = work.bytes / avg_call_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+        value, unit = gbs, "GB/s"
+    res = {
+        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if case.dtype == torch.bfloat16 else "f32", "data": "synthetic",
+        "config": {"workload": f"{name}: {DESCRIPTIONS[name]}", "num_splits": splits,
+                   "algorithmic_bytes": work.bytes, "algorithmic_flops": work.flops,
+                   "call_us_mean": round(float(call_ms.mean()) * 1e3, 2),
+                   "call_us_min": round(float(call_ms.min()) * 1e3, 2),
+                   "tflops": round(tflops, 3), "gbs": round(gbs, 2)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        _log("[bench] timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(case, name)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

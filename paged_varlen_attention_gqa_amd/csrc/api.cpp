@@ -1,0 +1,135 @@
+// C ABI of librelattn.so (declared in include/rel_attn.h): host-side argument
+// checks, split-count heuristic, workspace sizing and kernel dispatch.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/rel_attn.h"
+#include "kernels.h"
+
+using relattn::AttnParams;
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Query rows per work unit in the general kernel, and the decode tile.
+constexpr int kGeneralRows = 64;
+// Workgroups wanted in flight: 4 per compute unit on 256 CUs.
+constexpr int kTargetWorkgroups = 1024;
+// Fewest keys worth giving one split.
+constexpr int kMinKeysPerSplit = 256;
+constexpr int kMaxSplits = 128;
+
+bool supported_head_dim(int d) { return d == 64 || d == 128; }
+
+}  // namespace
+
+extern "C" int rel_attn_num_splits(int is_local, int batch_size, int max_query_len, int num_heads,
+                                   int num_kv_heads, int max_kv_len) {
+  if (batch_size < 1 || max_query_len < 1 || num_heads < 1 || num_kv_heads < 1 || max_kv_len < 0 ||
+      num_heads % num_kv_heads != 0)
+    return REL_ATTN_EINVAL;
+  if (is_local) return 1;
+  const int64_t G = num_heads / num_kv_heads;
+  const int64_t rows = (int64_t)max_query_len * G;
+  const int64_t qtiles = rows <= relattn::kDecodeMaxRows ? 1 : (rows + kGeneralRows - 1) / kGeneralRows;
+  const int64_t units = (int64_t)batch_size * num_kv_heads * qtiles;
+  int64_t splits = (kTargetWorkgroups + units - 1) / units;
+  const int64_t by_len = max_kv_len / kMinKeysPerSplit;
+  if (splits > by_len) splits = by_len;
+  if (splits > kMaxSplits) splits = kMaxSplits;
+  if (splits < 1) splits = 1;
+  return (int)splits;
+}
+
+extern "C" size_t rel_attn_workspace_bytes(int num_splits, int num_tokens, int num_heads, int head_dim) {
+  if (num_splits < 1 || num_tokens < 0 || num_heads < 1 || head_dim < 1) return 0;
+  if (num_splits == 1) return 0;
+  return (size_t)num_splits * (size_t)num_tokens * (size_t)num_heads * (size_t)(head_dim + 1) * 4u;
+}
+
+extern "C" const char* rel_attn_strerror(int code) {
+  switch (code) {
+    case REL_ATTN_OK: return "success";
+    case REL_ATTN_EINVAL: return "invalid argument";
+    case REL_ATTN_EUNSUPPORTED: return "unsupported dtype, head_dim, group size or block_size";
+    case REL_ATTN_EWORKSPACE: return "workspace missing or too small for num_splits > 1";
+    case REL_ATTN_ELAUNCH: return "HIP kernel launch failed";
+    default: return "unknown error code";
+  }
+}
+
+extern "C" int rel_attn_fwd(const void* q, const void* key_cache, const void* value_cache,
+                            const int32_t* block_table, const int32_t* cache_seqlens,
+                            const int32_t* cu_seqlens_q, const void* rel_logits, void* out, int dtype,
+                            int num_tokens, int batch_size, int max_seqlen_q, int max_blocks_per_seq,
+                            int num_heads, int num_kv_heads, int head_dim, int num_blocks, int block_size,
+                            int rel_extent, float softmax_scale, int causal, int window_left,
+                            int window_right, int num_splits, void* workspace, size_t workspace_bytes,
+                            size_t* workspace_needed, void* stream) {
+  // ---- argument checks (host only, before any launch) ----
+  if (num_tokens < 0 || batch_size < 0 || max_seqlen_q < 0 || max_blocks_per_seq < 0 || num_heads < 1 ||
+      num_kv_heads < 1 || head_dim < 1 || num_blocks < 0 || block_size < 1 || rel_extent < 0 ||
+      window_left < -1 || window_right < -1 || (causal != 0 && causal != 1))
+    return REL_ATTN_EINVAL;
+  if (num_heads % num_kv_heads != 0) return REL_ATTN_EINVAL;
+  if (num_splits < 1 || num_splits > kMaxSplits) return REL_ATTN_EINVAL;
+  if (!(softmax_scale == softmax_scale)) return REL_ATTN_EINVAL;  // NaN scale
+  if (dtype != REL_ATTN_FP32 && dtype != REL_ATTN_BF16) return REL_ATTN_EUNSUPPORTED;
+  if (!supported_head_dim(head_dim)) return REL_ATTN_EUNSUPPORTED;
+  const int G = num_heads / num_kv_heads;
+  if (G > 16) return REL_ATTN_EUNSUPPORTED;
+
+  const size_t need = rel_attn_workspace_bytes(num_splits, num_tokens, num_heads, head_dim);
+  if (workspace_needed) *workspace_needed = need;
+  if (workspace == nullptr && workspace_needed != nullptr) return REL_ATTN_OK;  // size query
+
+  if (batch_size > 0 && (cache_seqlens == nullptr || cu_seqlens_q == nullptr)) return REL_ATTN_EINVAL;
+  if (num_tokens > 0 && (q == nullptr || out == nullptr)) return REL_ATTN_EINVAL;
+  if (batch_size > 0 && num_tokens > 0 &&
+      (key_cache == nullptr || value_cache == nullptr || block_table == nullptr || num_blocks < 1 ||
+       max_blocks_per_seq < 1))
+    return REL_ATTN_EINVAL;
+  if (rel_extent > 0 && num_tokens > 0 && rel_logits == nullptr) return REL_ATTN_EINVAL;
+  if (batch_size > 65535 || num_kv_heads > 65535) return REL_ATTN_EUNSUPPORTED;
+  if (num_splits > 1) {
+    if (workspace == nullptr || workspace_bytes < need) return REL_ATTN_EWORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return REL_ATTN_EINVAL;
+  }
+  if (num_tokens == 0 || batch_size == 0 || max_seqlen_q == 0) return REL_ATTN_OK;
+
+  AttnParams P{};
+  P.q = q;
+  P.k = key_cache;
+  P.v = value_cache;
+  P.block_table = block_table;
+  P.seqlens_k = cache_seqlens;
+  P.cu_q = cu_seqlens_q;
+  P.rel = rel_logits;
+  P.out = out;
+  P.ws_o = num_splits > 1 ? reinterpret_cast<float*>(workspace) : nullptr;
+  P.ws_lse = num_splits > 1 ? P.ws_o + (size_t)num_splits * num_tokens * num_heads * head_dim : nullptr;
+  P.T = num_tokens;
+  P.B = batch_size;
+  P.max_q = max_seqlen_q;
+  P.max_blocks = max_blocks_per_seq;
+  P.H = num_heads;
+  P.Hkv = num_kv_heads;
+  P.G = G;
+  P.num_blocks = num_blocks;
+  P.bs = block_size;
+  P.E = rel_extent;
+  P.scale_log2 = softmax_scale * kLog2e;
+  P.causal = causal;
+  P.wl = window_left;
+  P.wr = window_right;
+  P.splits = num_splits;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int bf16 = dtype == REL_ATTN_BF16;
+  P.mode = 0;
+  if (relattn::launch_general(P, bf16, head_dim, s) != 0) return REL_ATTN_ELAUNCH;
+  if (num_splits > 1 && relattn::launch_combine(P, bf16, head_dim, s) != 0) return REL_ATTN_ELAUNCH;
+  return REL_ATTN_OK;
+}

@@ -1,0 +1,94 @@
+// Device-side helpers shared by the attention kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace relattn {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// Kernel arguments (one struct, passed by value).
+struct AttnParams {
+  const void* q;             // [T][H][D]
+  const void* k;             // [num_blocks][bs][Hkv][D]
+  const void* v;             // [num_blocks][bs][Hkv][D]
+  const int32_t* block_table;  // [B][max_blocks]
+  const int32_t* seqlens_k;  // [B]
+  const int32_t* cu_q;       // [B+1]
+  const void* rel;           // [T][H][E]
+  void* out;                 // [T][H][D]
+  float* ws_o;               // [splits][T][H][D]   (splits > 1)
+  float* ws_lse;             // [splits][T][H]      (splits > 1)
+  int T, B, max_q, max_blocks, H, Hkv, G, num_blocks, bs, E;
+  float scale_log2;          // softmax_scale * log2(e)
+  int causal, wl, wr, splits;
+  int mode;                  // general kernel: 0 = every request, 1 = only S_b*G > 16
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Two floats -> packed bf16 pair (round to nearest even, hardware convert).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2_t x = {lo, hi};
+  bf16x2_t y = __builtin_convertvector(x, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, y);
+}
+
+__device__ __forceinline__ float wave_max_xor_16_32(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_xor_16_32(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// Physical row (in units of D elements) of logical key j of request b, KV head g.
+__device__ __forceinline__ int64_t kv_row(const AttnParams& P, int b, int g, int j) {
+  int page = P.block_table[(int64_t)b * P.max_blocks + j / P.bs];
+  page = page < 0 ? 0 : (page >= P.num_blocks ? P.num_blocks - 1 : page);
+  return ((int64_t)page * P.bs + (j % P.bs)) * P.Hkv + g;
+}
+
+// Request b's first packed row t0, query count S and key count L, clamped so
+// that a malformed cu_seqlens_q / cache_seqlens can never index outside q,
+// out, rel_logits or the request's block-table row. Returns false when the
+// request has no rows.
+__device__ __forceinline__ bool request_bounds(const AttnParams& P, int b, int& t0, int& S, int& L) {
+  t0 = P.cu_q[b];
+  const int t1 = P.cu_q[b + 1];
+  if (t0 < 0 || t0 >= P.T || t1 <= t0) return false;
+  S = min(t1, P.T) - t0;
+  L = P.seqlens_k[b];
+  const int64_t cap = (int64_t)P.max_blocks * P.bs;
+  L = L < 0 ? 0 : (int)((int64_t)L > cap ? cap : L);
+  return true;
+}
+
+// Visible key range [lo, hi) of absolute query position p in a request of L keys.
+__device__ __forceinline__ void visible_range(const AttnParams& P, int p, int L, int& lo, int& hi) {
+  lo = 0;
+  hi = L;
+  if (P.causal) hi = min(hi, p + 1);
+  if (P.wl >= 0) lo = max(lo, p - P.wl);
+  if (P.wr >= 0) hi = min(hi, p + P.wr + 1);
+  if (hi < lo) hi = lo;
+}
+
+}  // namespace relattn

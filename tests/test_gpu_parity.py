@@ -1,0 +1,178 @@
+"""Parity of the HIP path with the fp64 oracle on the same seeded inputs.
+
+Small and reduced-size workloads are compared on every output; the full-size
+workloads (the sizes the benchmark times, in its launch configuration) are
+compared on every output the oracle finishes quickly and on sampled rows
+otherwise.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL, compare, device_case, log, run_gpu
+from paged_varlen_attention_gqa_amd.inputs import config_spec, make_case, make_config
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    from paged_varlen_attention_gqa_amd import load_library
+
+    load_library()  # fails loudly when librelattn.so is missing
+
+
+def _check(case, tokens=None, what=None, **over):
+    what = what or case.name
+    log(f"[parity] {what}: T={case.num_tokens} H={case.num_heads} Hkv={case.num_kv_heads} "
+        f"D={case.head_dim} bs={case.block_size} E={case.rel_extent} over={over}")
+    got = run_gpu(case, **over)
+    ref = oracle.oracle_attention(**case.kwargs(), tokens=tokens)
+    return compare(got, ref, case.dtype, tokens=tokens, what=what)
+
+
+# ---- the five workloads at reduced size (every output) ----
+REDUCED = [("tiny_fp32", 1.0), ("decode_b64", 1 / 8), ("prefill_chunked", 1 / 8),
+           ("mixed_window", 1 / 8), ("decode_long_b1", 1 / 16)]
+
+
+@pytest.mark.parametrize("name,scale", REDUCED, ids=[n for n, _ in REDUCED])
+def test_reduced(name, scale):
+    _check(make_config(name, scale=scale), what=f"{name}@{scale:g}")
+
+
+# ---- full-size workloads ----
+def test_full_tiny_fp32():
+    _check(make_config("tiny_fp32"))
+
+
+def test_full_decode_b64():
+    _check(make_config("decode_b64"))
+
+
+def test_full_decode_long_b1():
+    _check(make_config("decode_long_b1"))
+
+
+def test_full_prefill_chunked_sampled():
+    case = make_config("prefill_chunked")
+    cu = case.cu_seqlens_q.tolist()
+    rng = np.random.default_rng(0)
+    tokens = set()
+    for b in range(case.batch_size):
+        S = cu[b + 1] - cu[b]
+        for i in list(rng.choice(S, 6, replace=False)) + [0, S - 1]:
+            tokens.add(cu[b] + int(i))
+    _check(case, tokens=tokens, what="prefill_chunked sampled")
+
+
+def test_full_mixed_window_sampled():
+    case = make_config("mixed_window")
+    cu = case.cu_seqlens_q.tolist()
+    rng = np.random.default_rng(1)
+    tokens = set(range(cu[8], cu[-1]))  # every decode token
+    for b in range(8):
+        S = cu[b + 1] - cu[b]
+        for i in list(rng.choice(S, 3, replace=False)) + [0, S - 1]:
+            tokens.add(cu[b] + int(i))
+    _check(case, tokens=tokens, what="mixed_window sampled")
+
+
+# ---- edge cases ----
+EDGE = [
+    dict(name="g1_noncausal", query_lens=[3, 40], kv_lens=[50, 40], num_heads=4, num_kv_heads=4,
+         head_dim=128, block_size=16, rel_extent=20, causal=False),
+    dict(name="g16_window_both", query_lens=[5, 1, 70], kv_lens=[130, 77, 200], num_heads=32,
+         num_kv_heads=2, head_dim=128, block_size=16, rel_extent=50, causal=False, window_size=(33, 9)),
+    dict(name="d64_bs64", query_lens=[1, 9, 33], kv_lens=[300, 65, 129], num_heads=8, num_kv_heads=2,
+         head_dim=64, block_size=64, rel_extent=100),
+    dict(name="odd_block_size", query_lens=[2, 17], kv_lens=[45, 99], num_heads=8, num_kv_heads=4,
+         head_dim=128, block_size=7, rel_extent=13),
+    dict(name="block_size_1", query_lens=[4, 1], kv_lens=[20, 31], num_heads=4, num_kv_heads=2,
+         head_dim=64, block_size=1, rel_extent=8),
+    dict(name="no_bias", query_lens=[6, 1], kv_lens=[66, 1000], num_heads=16, num_kv_heads=4,
+         head_dim=128, block_size=16, rel_extent=0),
+    dict(name="extent_beyond_len", query_lens=[8, 1], kv_lens=[30, 41], num_heads=8, num_kv_heads=8,
+         head_dim=128, block_size=16, rel_extent=500),
+    dict(name="empty_request", query_lens=[0, 5, 0, 1], kv_lens=[10, 5, 0, 3], num_heads=8,
+         num_kv_heads=2, head_dim=128, block_size=16, rel_extent=4),
+    dict(name="window_left_only", query_lens=[64, 1], kv_lens=[256, 900], num_heads=8, num_kv_heads=1,
+         head_dim=128, block_size=16, rel_extent=64, window_size=(100, -1)),
+    dict(name="fp32_d128_window", query_lens=[3, 20], kv_lens=[77, 20], num_heads=6, num_kv_heads=3,
+         head_dim=128, block_size=16, rel_extent=40, window_size=(10, 0), dtype=torch.float32),
+    dict(name="fp32_noncausal_g4", query_lens=[1, 7], kv_lens=[90, 7], num_heads=8, num_kv_heads=2,
+         head_dim=64, block_size=8, rel_extent=5, causal=False, dtype=torch.float32),
+]
+
+
+@pytest.mark.parametrize("spec", EDGE, ids=[e["name"] for e in EDGE])
+def test_edge(spec):
+    spec = dict(spec)
+    spec.setdefault("pool_pages", None)
+    _check(make_case(**spec))
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 8, 37, 128])
+def test_split_counts(splits):
+    case = make_case(name="splits", query_lens=[1, 1, 4, 1], kv_lens=[3000, 17, 700, 5000],
+                     num_heads=16, num_kv_heads=4, head_dim=128, block_size=16, rel_extent=600)
+    _check(case, num_splits=splits, what=f"splits={splits}")
+
+
+def test_max_seqlen_bucketed():
+    """A loose max_seqlen_q bound (next power of two, and more) gives the same output."""
+    case = make_case(name="bucket", query_lens=[5, 17, 1], kv_lens=[40, 90, 20], num_heads=8,
+                     num_kv_heads=2, head_dim=128, block_size=16, rel_extent=32)
+    a = run_gpu(case)
+    b = run_gpu(case, max_seqlen_q=32)
+    c = run_gpu(case, max_seqlen_q=1000)
+    assert torch.equal(a, b) and torch.equal(a, c)
+
+
+def test_page_permutation_bitwise():
+    """Moving pages to other physical slots (and relabelling the table) changes no bit."""
+    case = make_case(name="perm", query_lens=[1, 30, 2], kv_lens=[500, 300, 1200], num_heads=16,
+                     num_kv_heads=4, head_dim=128, block_size=16, rel_extent=256, pool_pages=200)
+    a = run_gpu(case)
+    g = torch.Generator().manual_seed(7)
+    perm = torch.randperm(case.key_cache.shape[0], generator=g)
+    kc = torch.empty_like(case.key_cache)
+    vc = torch.empty_like(case.value_cache)
+    kc[perm] = case.key_cache
+    vc[perm] = case.value_cache
+    bt = perm[case.block_table.long()].to(torch.int32)
+    b = run_gpu(case, key_cache=kc.cuda(), value_cache=vc.cuda(), block_table=bt.cuda())
+    assert torch.equal(a, b)
+
+
+def test_kv_shorter_than_queries_gives_zero_rows():
+    """Rows whose position is negative (L_b < S_b) see no key and come out as zeros."""
+    case = make_case(name="short", query_lens=[4], kv_lens=[4], num_heads=4, num_kv_heads=2,
+                     head_dim=128, block_size=16, rel_extent=4)
+    kw = device_case(case)
+    kw["cache_seqlens"] = torch.tensor([2], dtype=torch.int32, device="cuda")
+    from paged_varlen_attention_gqa_amd import rel_attn_fwd
+
+    out = rel_attn_fwd(**kw)
+    torch.cuda.synchronize()
+    ref_kw = case.kwargs()
+    ref_kw["cache_seqlens"] = torch.tensor([2], dtype=torch.int32)
+    ref = oracle.oracle_attention(**ref_kw)
+    compare(out, ref, case.dtype, what="L<S")
+    assert torch.count_nonzero(out[:2]) == 0
+
+
+def test_preallocated_out_and_determinism():
+    case = make_config("decode_b64", scale=1 / 16)
+    kw = device_case(case)
+    from paged_varlen_attention_gqa_amd import rel_attn_fwd
+
+    out = torch.full_like(kw["q"], float("nan"))
+    r = rel_attn_fwd(**kw, out=out)
+    assert r.data_ptr() == out.data_ptr()
+    r2 = rel_attn_fwd(**kw)
+    torch.cuda.synchronize()
+    assert torch.equal(r, r2)
