@@ -126,10 +126,42 @@ extern "C" int rel_attn_fwd(const void* q, const void* key_cache, const void* va
   P.wr = window_right;
   P.splits = num_splits;
 
+  {
+    const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
+    P.kv_cap = cap > 0x7fffffff ? 0x7fffffff : (int)cap;
+  }
+  P.bs_log2 = -1;
+  for (int k = 0; k < 31; ++k)
+    if ((1 << k) == block_size) P.bs_log2 = k;
+  // Keys per split of the decode kernel: the longest key range a request can
+  // have (its page-table capacity, or the window span) cut into num_splits
+  // pieces of whole 16-key tiles.
+  {
+    int64_t span = (int64_t)max_blocks_per_seq * block_size;
+    if (window_left >= 0) {
+      const int64_t right = window_right >= 0 ? window_right : (causal ? 0 : span);
+      const int64_t w = (int64_t)window_left + right + max_seqlen_q + 16;
+      if (w < span) span = w;
+    }
+    int64_t chunk = (span + num_splits - 1) / num_splits;
+    chunk = (chunk + 15) / 16 * 16;
+    if (chunk < 16) chunk = 16;
+    P.dec_chunk = chunk > (1 << 30) ? (1 << 30) : (int)chunk;
+  }
+
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int bf16 = dtype == REL_ATTN_BF16;
-  P.mode = 0;
-  if (relattn::launch_general(P, bf16, head_dim, s) != 0) return REL_ATTN_ELAUNCH;
+  if (relattn::decode_supported(P, bf16, head_dim)) {
+    if (relattn::launch_decode(P, head_dim, s) != 0) return REL_ATTN_ELAUNCH;
+    // requests with more than 16 packed rows go to the general kernel
+    P.mode = 1;
+    if ((int64_t)max_seqlen_q * G > relattn::kDecodeMaxRows &&
+        relattn::launch_general(P, bf16, head_dim, s) != 0)
+      return REL_ATTN_ELAUNCH;
+  } else {
+    P.mode = 0;
+    if (relattn::launch_general(P, bf16, head_dim, s) != 0) return REL_ATTN_ELAUNCH;
+  }
   if (num_splits > 1 && relattn::launch_combine(P, bf16, head_dim, s) != 0) return REL_ATTN_ELAUNCH;
   return REL_ATTN_OK;
 }

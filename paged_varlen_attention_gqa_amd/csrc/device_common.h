@@ -34,6 +34,9 @@ struct AttnParams {
   float scale_log2;          // softmax_scale * log2(e)
   int causal, wl, wr, splits;
   int mode;                  // general kernel: 0 = every request, 1 = only S_b*G > 16
+  int dec_chunk;             // decode kernel: keys per split (multiple of 16)
+  int bs_log2;               // log2(block_size) when it is a power of two, else -1
+  int kv_cap;                // keys a block-table row can address: min(max_blocks * bs, 2^31 - 1)
 };
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
@@ -76,8 +79,7 @@ __device__ __forceinline__ bool request_bounds(const AttnParams& P, int b, int& 
   if (t0 < 0 || t0 >= P.T || t1 <= t0) return false;
   S = min(t1, P.T) - t0;
   L = P.seqlens_k[b];
-  const int64_t cap = (int64_t)P.max_blocks * P.bs;
-  L = L < 0 ? 0 : (int)((int64_t)L > cap ? cap : L);
+  L = L < 0 ? 0 : (L > P.kv_cap ? P.kv_cap : L);
   return true;
 }
 

@@ -10,6 +10,8 @@ namespace relattn {
 // Each returns 0 on success, -1 when the launch was rejected.
 int launch_general(const AttnParams& P, int dtype_bf16, int head_dim, hipStream_t stream);
 int launch_decode(const AttnParams& P, int head_dim, hipStream_t stream);
+// Whether the decode kernel handles this call's dtype / head_dim / block_size.
+bool decode_supported(const AttnParams& P, int dtype_bf16, int head_dim);
 int launch_combine(const AttnParams& P, int dtype_bf16, int head_dim, hipStream_t stream);
 
 // Largest S_b * G the decode kernel handles (one 16-row MFMA tile).
