@@ -19,6 +19,10 @@ constexpr int kGeneralRows = 64;
 constexpr int kTargetWorkgroups = 1024;
 // Fewest keys worth giving one split.
 constexpr int kMinKeysPerSplit = 256;
+// Decode-shaped calls (one 16-column tile of query rows per KV head): about
+// 16 workgroups per compute unit, at least 1024 keys per split.
+constexpr int kDecodeTargetWorkgroups = 4096;
+constexpr int kDecodeMinKeysPerSplit = 1024;
 constexpr int kMaxSplits = 128;
 
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
@@ -33,10 +37,16 @@ extern "C" int rel_attn_num_splits(int is_local, int batch_size, int max_query_l
   if (is_local) return 1;
   const int64_t G = num_heads / num_kv_heads;
   const int64_t rows = (int64_t)max_query_len * G;
-  const int64_t qtiles = rows <= relattn::kDecodeMaxRows ? 1 : (rows + kGeneralRows - 1) / kGeneralRows;
+  const bool decode = rows <= relattn::kDecodeMaxRows;
+  const int64_t qtiles = decode ? 1 : (rows + kGeneralRows - 1) / kGeneralRows;
   const int64_t units = (int64_t)batch_size * num_kv_heads * qtiles;
-  int64_t splits = (kTargetWorkgroups + units - 1) / units;
-  const int64_t by_len = max_kv_len / kMinKeysPerSplit;
+  // Decode-shaped calls stream K/V at memory speed: many short splits keep
+  // every compute unit fed despite unequal request lengths. Prefill-shaped
+  // calls have work enough in their query tiles.
+  const int64_t target = decode ? kDecodeTargetWorkgroups : kTargetWorkgroups;
+  const int64_t min_keys = decode ? kDecodeMinKeysPerSplit : kMinKeysPerSplit;
+  int64_t splits = (target + units - 1) / units;
+  const int64_t by_len = max_kv_len / min_keys;
   if (splits > by_len) splits = by_len;
   if (splits > kMaxSplits) splits = kMaxSplits;
   if (splits < 1) splits = 1;

@@ -50,16 +50,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, y);
 }
 
+// Reductions over the four lanes l, l^16, l^32, l^48 (same l%16) of a wave,
+// with the gfx950 lane-swap instructions (VALU only, no LDS round trip):
+// permlane32_swap on two copies of v yields v[l%32] and v[32 + l%32] in every
+// lane, permlane16_swap likewise for the 16-lane rows.
 __device__ __forceinline__ float wave_max_xor_16_32(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  const uint32_t u = __float_as_uint(v);
+  auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(v);
+  auto c = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 
 __device__ __forceinline__ float wave_sum_xor_16_32(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  const uint32_t u = __float_as_uint(v);
+  auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t w = __float_as_uint(v);
+  auto c = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
 // Physical row (in units of D elements) of logical key j of request b, KV head g.
