@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "librelattn.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["api.cpp", "attn_general.hip", "attn_decode.hip", "combine.hip"]
+SOURCES = ["api.cpp", "attn_general.hip", "attn_decode.hip", "attn_prefill.hip", "combine.hip"]
 ARCH = "gfx950"
 
 

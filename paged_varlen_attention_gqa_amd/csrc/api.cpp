@@ -165,9 +165,11 @@ extern "C" int rel_attn_fwd(const void* q, const void* key_cache, const void* va
     if (relattn::launch_decode(P, head_dim, s) != 0) return REL_ATTN_ELAUNCH;
     // requests with more than 16 packed rows go to the general kernel
     P.mode = 1;
-    if ((int64_t)max_seqlen_q * G > relattn::kDecodeMaxRows &&
-        relattn::launch_general(P, bf16, head_dim, s) != 0)
-      return REL_ATTN_ELAUNCH;
+    if ((int64_t)max_seqlen_q * G > relattn::kDecodeMaxRows) {
+      const int rc = relattn::prefill_supported(P, bf16, head_dim) ? relattn::launch_prefill(P, s)
+                                                                   : relattn::launch_general(P, bf16, head_dim, s);
+      if (rc != 0) return REL_ATTN_ELAUNCH;
+    }
   } else {
     P.mode = 0;
     if (relattn::launch_general(P, bf16, head_dim, s) != 0) return REL_ATTN_ELAUNCH;

@@ -1,0 +1,440 @@
+// Prefill attention kernel: requests with more than 16 packed query rows,
+// bf16, head_dim 128, block_size a power of two that is a multiple of 16.
+//
+// A workgroup (8 waves) owns 256 packed rows of one (request, KV head): row
+// r is token r / G and query head kv_head * G + r % G, so the G query heads
+// that share a KV head share every K/V tile. Wave w owns rows 32w..32w+31
+// as the 32 columns of S^T = K Q^T. Per 64-key tile:
+//   * buffer-to-LDS loads copy the K/V tile (shared by the workgroup) and
+//     each wave's slice of relative bias into LDS, double buffered, one tile
+//     ahead of the arithmetic;
+//   * K rows are stored permuted inside each 32-key half: LDS row
+//     m = 8i + 4h + k holds key 16h + 4i + k, so that output register a of
+//     lane (h, n) of v_mfma_f32_32x32x16_bf16 is key 16h + a: every lane owns
+//     16 consecutive keys of its query column, and their bias values are 16
+//     consecutive entries of one rel_logits row (copied as two unaligned
+//     16-byte pieces to aligned LDS slots);
+//   * V^T operands come from the row-major V tile through the LDS transpose
+//     read (lane (g, i) of a 16-lane group receives V[4g + k][col0 + i]);
+//     O^T += V^T P^T takes the S^T registers as its B operand directly;
+//   * softmax in the S^T layout: each query column lives in two lanes
+//     (l and l ^ 32), so a row max or sum is one lane swap.
+// Chunks of every K/V row in LDS are XOR-swizzled so that the K operand
+// reads and the transpose reads are free of bank conflicts.
+//
+// Score and bias rule: prhub.com.cn report on vLLM PR #48858, "key source
+// snippets" (score_mod_rel_bias); tensor layouts: docs.vllm.ai
+// inkling_fa4_rel_attention.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace relattn {
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kWaves = 8;
+constexpr int kRowsWG = 32 * kWaves;  // packed query rows per workgroup
+constexpr int kKeys = 64;             // keys per tile
+constexpr int kRowBytes = kD * 2;
+constexpr int kHalf = kKeys * kRowBytes;  // K (or V) part of a tile: 16 KB
+constexpr int kKV = 2 * kHalf;            // 32 KB
+constexpr int kBiasWave = 32 * kKeys * 2;  // one wave's bias slice of a tile: 4 KB
+constexpr float kRescaleSlack = 8.0f;     // log2 units, as in the decode kernel
+
+typedef __bf16 bf16x8v_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// chunk swizzle of K/V LDS row r: a bijection of 0..15 that keeps 16
+// consecutive rows on distinct chunks and maps rows 4a..4a+3 to chunks that
+// differ in bits 1..3
+__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds, 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ float lane_swap32_max(float v) {
+  const uint32_t u = __float_as_uint(v);
+  auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+__device__ __forceinline__ float lane_swap32_sum(float v) {
+  const uint32_t u = __float_as_uint(v);
+  auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
+__global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P) {
+  // one LDS object per buffer, so that the compiler waits for exactly the
+  // copies a read depends on
+  __shared__ __attribute__((aligned(1024))) char kv0[kKV];
+  __shared__ __attribute__((aligned(1024))) char kv1[kKV];
+  __shared__ __attribute__((aligned(1024))) char bias0[kWaves * kBiasWave];
+  __shared__ __attribute__((aligned(1024))) char bias1[kWaves * kBiasWave];
+
+  const int b = blockIdx.z;
+  const int g = blockIdx.y;
+  const int qtiles = gridDim.x / P.splits;
+  // longest query tiles (largest causal key range) first
+  const int qt = qtiles - 1 - (int)(blockIdx.x / P.splits);
+  const int split = blockIdx.x % P.splits;
+  int t0, S, L;
+  if (!request_bounds(P, b, t0, S, L)) return;
+  const int G = P.G;
+  const int nrows = S * G;
+  if (nrows <= 16) return;  // the decode kernel handles these
+  const int r0 = qt * kRowsWG;
+  if (r0 >= nrows) return;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n = lane & 31;  // query column of this lane (within the wave)
+  const int h = lane >> 5;  // which 16 keys of a 32-key half this lane holds
+
+  const int r = r0 + 32 * wave + n;
+  const bool row_ok = r < nrows;
+  const int itok = row_ok ? r / G : 0;
+  const int hq = g * G + (row_ok ? r % G : 0);
+  const int t = t0 + itok;
+  const int p = itok + L - S;
+  int row_lo = 0, row_hi = 0;
+  if (row_ok) visible_range(P, p, L, row_lo, row_hi);
+
+  // key range of the workgroup (union of its rows)
+  const int ia = r0 / G;
+  const int ib = (min(r0 + kRowsWG, nrows) - 1) / G;
+  int lo_a, hi_a, lo_b, hi_b;
+  visible_range(P, ia + L - S, L, lo_a, hi_a);
+  visible_range(P, ib + L - S, L, lo_b, hi_b);
+  const int wg_lo = min(lo_a, lo_b);
+  const int wg_hi = max(hi_a, hi_b);
+  const int lo_max = max(lo_a, lo_b);  // every row sees [lo_max, hi_min)
+  const int hi_min = min(hi_a, hi_b);
+  const int kstart = wg_lo & ~(kKeys - 1);
+  const int ntiles = wg_hi > wg_lo ? (wg_hi - kstart + kKeys - 1) / kKeys : 0;
+  const int tps = (ntiles + P.splits - 1) / P.splits;
+  const int tile_begin = __builtin_amdgcn_readfirstlane(split * tps);
+  const int tile_end = __builtin_amdgcn_readfirstlane(min(ntiles, tile_begin + tps));
+
+  // Q^T as the B operand: lane (h, n) holds dims 16kk + 8h .. +7 of its row
+  u32x4_t qreg[kD / 16];
+  {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(P.q) + ((int64_t)t * P.H + hq) * kD;
+#pragma unroll
+    for (int kk = 0; kk < kD / 16; ++kk) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (row_ok) v = *reinterpret_cast<const u32x4_t*>(qp + 16 * kk + 8 * h);
+      qreg[kk] = v;
+    }
+  }
+
+  // ---- K/V copy geometry ----
+  // wave w copies keys 8w..8w+7 of the tile (inside one page segment) with
+  // two instructions for K and two for V; instruction c4 covers keys
+  // 8w + 4c4 + (0..3), lane l one 16-byte chunk of key 8w + 4c4 + l/16.
+  // K key 32st + 16h' + 4i + kk goes to LDS row 32st + 8i + 4h' + kk.
+  const uint32_t row_bytes = (uint32_t)P.Hkv * kD * 2;
+  uint32_t k_src[2], v_src[2];
+  int k_dst[2], v_dst[2];
+#pragma unroll
+  for (int c4 = 0; c4 < 2; ++c4) {
+    const int key = 8 * wave + 4 * c4;  // first key of the instruction (tile-relative)
+    const int st = key >> 5, kap = key & 31;
+    const int krow0 = 32 * st + 8 * ((kap & 15) >> 2) + 4 * (kap >> 4);
+    const int krow = krow0 + (lane >> 4);
+    const int vrow = key + (lane >> 4);
+    k_src[c4] = (uint32_t)(4 * c4 + (lane >> 4)) * row_bytes + 16u * (uint32_t)((lane & 15) ^ swz(krow));
+    v_src[c4] = (uint32_t)(4 * c4 + (lane >> 4)) * row_bytes + 16u * (uint32_t)((lane & 15) ^ swz(vrow));
+    k_dst[c4] = krow0 * kRowBytes;
+    v_dst[c4] = kHalf + key * kRowBytes;
+  }
+  // K operand read of step kk: row 32st + n, logical chunk 2kk + h; the
+  // chunk is (2kk) ^ (h ^ swz(n)) as 2kk and h occupy disjoint bits
+  uint32_t k_rd[kD / 16];
+#pragma unroll
+  for (int kk = 0; kk < kD / 16; ++kk)
+    k_rd[kk] = (uint32_t)(n * kRowBytes + 16 * ((2 * kk) ^ (h ^ swz(n & 15))));
+  // transpose reads of V for (half st, block kb, dim tile mt, group sr): lane
+  // (h, n), j = n%16, points at row 32st + 16h + 8kb + 4sr + j/4 and element
+  // 32mt + 16(n/16) + 4(j%4). The row's swizzle is 8sr + 2(j/4) + kb, so the
+  // chunk is Y ^ (4mt ^ 8sr ^ kb) with Y = 2(n/16) + (j%4)/2 ^ 2(j/4): one
+  // lane value XOR a constant of (mt, sr, kb).
+  uint32_t v_rd[8];  // index: kb | (mt&1)<<1 | ((mt>>1)^sr)<<2
+  {
+    const int j = n & 15;
+    const int Y = (2 * (n >> 4) + ((j & 3) >> 1)) ^ (2 * (j >> 2));
+    const uint32_t base = (uint32_t)((16 * h + (j >> 2)) * kRowBytes + 8 * (j & 1));
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int C = (c & 1) | ((c >> 1) & 1) << 2 | ((c >> 2) & 1) << 3;
+      v_rd[c] = base + 16u * (uint32_t)(Y ^ C);
+    }
+  }
+
+  const int bs_log2 = P.bs_log2;
+  const int bs_mask = P.bs - 1;
+  const int32_t* bt_row = P.block_table + (int64_t)b * P.max_blocks;
+  const int last_page = ((L > 0 ? L : 1) - 1) >> bs_log2;
+  const char* kbytes = reinterpret_cast<const char*>(P.k);
+  const char* vbytes = reinterpret_cast<const char*>(P.v);
+  const int64_t head_bytes = (int64_t)g * kD * 2;
+
+  // ---- relative-bias copy geometry ----
+  // The wave's slice of a tile: for each (half st, lane half h) the 16
+  // entries d = p - (j0 + 32st + 16h) - 15 .. +15 of each of its 32 rows,
+  // as two 8-entry pieces. LDS layout [st][h][piece][row n] x 16 bytes, so
+  // instruction q = 2st + h writes 1 KB in lane order (lane = piece*32 + n).
+  // Copies read through one resource over the wave's rows plus 64 entries
+  // on each side (inside the tensor); pieces outside it read as zeros.
+  const int E = P.E;
+  const int64_t tensor_elems = (int64_t)P.T * P.H * E;
+  int64_t reg_lo = 0, reg_hi = 0;
+  {
+    const int rw0 = min(r0 + 32 * wave, nrows - 1), rw1 = min(r0 + 32 * wave + 31, nrows - 1);
+    const int64_t row_min = (int64_t)(t0 + rw0 / G) * P.H + g * G;
+    const int64_t row_max = (int64_t)(t0 + rw1 / G) * P.H + g * G + G - 1;
+    reg_lo = row_min * E - 64;
+    reg_hi = (row_max + 1) * E + 64;
+    reg_lo = reg_lo < 0 ? 0 : reg_lo;
+    reg_hi = reg_hi > tensor_elems ? tensor_elems : reg_hi;
+    if (E == 0) reg_lo = reg_hi = 0;
+  }
+  const char* rel_base = E > 0 ? reinterpret_cast<const char*>(P.rel) + reg_lo * 2 : reinterpret_cast<const char*>(P.q);
+  const __amdgpu_buffer_rsrc_t rel_rsrc = make_rsrc(rel_base, (uint32_t)((reg_hi - reg_lo) * 2));
+  // As a copy lane, lane piece*32 + n loads a piece of column n's row, with
+  // column n's position p (lanes n and n + 32 share the column). Pieces can
+  // straddle the resource only at the two ends of the whole tensor: lanes of
+  // the first or last tensor row fix their values in registers.
+  const int64_t my_row_abs = (int64_t)t * P.H + hq;
+  const int rel_lane_elem = (int)(my_row_abs * E - reg_lo);  // row start, relative to the resource
+  const int piece = lane >> 5;
+  const bool edge_row = E > 0 && row_ok && (my_row_abs == 0 || my_row_abs == (int64_t)P.T * P.H - 1);
+
+  auto issue = [&](char* kv, char* bias, int j0) {
+    const int key0 = j0 + 8 * wave;
+    int pidx = key0 >> bs_log2;
+    pidx = pidx > last_page ? last_page : pidx;  // keys past L: any valid page of the request
+    int page = bt_row[pidx];
+    page = page < 0 ? 0 : (page >= P.num_blocks ? P.num_blocks - 1 : page);
+    page = __builtin_amdgcn_readfirstlane(page);
+    const int64_t base = (((int64_t)page << bs_log2) + (key0 & bs_mask)) * row_bytes + head_bytes;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbytes + base, 0x7fffffffu);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbytes + base, 0x7fffffffu);
+#pragma unroll
+    for (int c4 = 0; c4 < 2; ++c4) dma16(kr, kv + k_dst[c4], k_src[c4]);
+#pragma unroll
+    for (int c4 = 0; c4 < 2; ++c4) dma16(vr, kv + v_dst[c4], v_src[c4]);
+    char* my_bias = bias + wave * kBiasWave;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int st = q >> 1, hh = q & 1;
+      const int e_lo = p - (j0 + 32 * st + 16 * hh) - 15 + 8 * piece;
+      dma16(rel_rsrc, my_bias + 1024 * q, (uint32_t)(rel_lane_elem + e_lo) * 2u);
+    }
+    asm volatile("" ::: "memory");
+  };
+
+  f32x16_t oacc[kD / 32];  // O^T: dim tile mt, lane (h, n) reg a = dim 32mt + 8(a/4) + 4h + a%4
+#pragma unroll
+  for (int mt = 0; mt < kD / 32; ++mt)
+#pragma unroll
+    for (int a = 0; a < 16; ++a) oacc[mt][a] = 0.f;
+  float m_ref = kNegInf;  // running reference max of the column (log2 units)
+  float l_part = 0.f;     // this lane's share of the column sum
+  const float scale_log2 = P.scale_log2;
+
+  auto compute = [&](const char* kv, const char* bias, int j0) {
+    // S^T = K Q^T for the two 32-key halves
+    f32x16_t s[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+      for (int a = 0; a < 16; ++a) s[st][a] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < kD / 16; ++kk) {
+        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kv + 32 * st * kRowBytes + k_rd[kk]);
+        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, kf),
+                                                        __builtin_bit_cast(bf16x8v_t, qreg[kk]), s[st], 0, 0, 0);
+      }
+    }
+    // bias runs: entries 0..15 of half st, from the smallest distance up
+    const char* my_bias = bias + wave * kBiasWave;
+    u32x4_t bv[2][2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int pc = 0; pc < 2; ++pc)
+        bv[st][pc] = *reinterpret_cast<const u32x4_t*>(my_bias + 1024 * (2 * st + h) + 16 * (32 * pc + n));
+    if (__builtin_amdgcn_ballot_w64(edge_row) != 0) {
+      // rows at the very start or end of the tensor: re-read their in-range
+      // entries one by one
+      if (edge_row) {
+        const uint16_t* rrow = reinterpret_cast<const uint16_t*>(P.rel) + my_row_abs * E;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) {
+            const int d = p - (j0 + 32 * st + 16 * h) - 15 + x;
+            if (d >= 0 && d < E) {
+              const uint32_t v = rrow[d];
+              const uint32_t w = bv[st][x >> 3][(x >> 1) & 3];
+              bv[st][x >> 3][(x >> 1) & 3] = (x & 1) ? ((w & 0xffffu) | (v << 16)) : ((w & 0xffff0000u) | v);
+            }
+          }
+      }
+    }
+    // scale, bias, mask (log2 units); register a of half st is key j0 + 32st + 16h + a
+    const bool interior = (j0 >= lo_max) && (j0 + kKeys <= hi_min);
+    float mx = kNegInf;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int jb = j0 + 32 * st + 16 * h;
+      const int dtop = p - jb;  // distance of register 0
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const int x = 15 - a;  // entry of the run
+        const uint32_t w = bv[st][x >> 3][(x >> 1) & 3];
+        const uint32_t in_range = (uint32_t)(dtop - a) < (uint32_t)E ? 0xffffffffu : 0u;
+        const float bias_v = __uint_as_float(((x & 1) ? (w & 0xffff0000u) : (w << 16)) & in_range);
+        float v = fmaf(s[st][a], scale_log2, bias_v * kLog2e);
+        if (!interior) {
+          const int j = jb + a;
+          v = (j >= row_lo && j < row_hi) ? v : kNegInf;
+        } else {
+          v = row_ok ? v : kNegInf;
+        }
+        s[st][a] = v;
+        mx = fmaxf(mx, v);
+      }
+    }
+    mx = lane_swap32_max(mx);
+    if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = m_ref == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_part *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < kD / 32; ++mt) oacc[mt] *= alpha;
+    }
+    const float m_use = m_ref == kNegInf ? 0.f : m_ref;
+    // keys past L may hold anything (NaN) and 0 * NaN = NaN: zero their V
+    // elements in the operand
+    const bool tail = j0 + kKeys > L;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      // probabilities as the B operand of PV: block kb takes registers 8kb..8kb+7
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const float e = __builtin_amdgcn_exp2f(s[st][a] - m_use);
+        s[st][a] = e;
+        l_part += e;
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const u32x4_t pb = {pack_bf16x2(s[st][8 * kb + 0], s[st][8 * kb + 1]), pack_bf16x2(s[st][8 * kb + 2], s[st][8 * kb + 3]),
+                            pack_bf16x2(s[st][8 * kb + 4], s[st][8 * kb + 5]), pack_bf16x2(s[st][8 * kb + 6], s[st][8 * kb + 7])};
+#pragma unroll
+        for (int mt = 0; mt < kD / 32; ++mt) {
+          u32x2_t part[2];
+#pragma unroll
+          for (int sr = 0; sr < 2; ++sr) {
+            const int c = kb | ((mt & 1) << 1) | ((((mt >> 1) ^ sr) & 1) << 2);
+            const char* addr = kv + kHalf + (32 * st + 8 * kb + 4 * sr) * kRowBytes + v_rd[c];
+            part[sr] = __builtin_bit_cast(
+                u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)addr));
+            if (tail) {
+              // this lane received keys 32st + 16h + 8kb + 4sr + (0..3)
+              const int k0 = j0 + 32 * st + 16 * h + 8 * kb + 4 * sr;
+              part[sr][0] &= (k0 < L ? 0xffffu : 0u) | (k0 + 1 < L ? 0xffff0000u : 0u);
+              part[sr][1] &= (k0 + 2 < L ? 0xffffu : 0u) | (k0 + 3 < L ? 0xffff0000u : 0u);
+            }
+          }
+          const u32x4_t av = {part[0][0], part[0][1], part[1][0], part[1][1]};
+          oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, av),
+                                                             __builtin_bit_cast(bf16x8v_t, pb), oacc[mt], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // ---- key loop, double buffered: tile it+1 is copied while tile it is used ----
+  // The copies for the next tile are issued unconditionally (the last tile
+  // is re-read) so that the compiler's wait counts stay exact.
+  if (tile_begin < tile_end) {
+    const int last = tile_end - 1;
+    issue(kv0, bias0, kstart + kKeys * tile_begin);
+    for (int it = tile_begin; it < tile_end; it += 2) {
+      const int jA = kstart + kKeys * it;
+      const int jB = kstart + kKeys * min(it + 1, last);
+      issue(kv1, bias1, jB);
+      __syncthreads();  // buffer 0 holds tile it for every wave
+      compute(kv0, bias0, jA);
+      __syncthreads();  // everyone is done with buffer 0
+      if (it + 1 >= tile_end) break;
+      const int jC = kstart + kKeys * min(it + 2, last);
+      issue(kv0, bias0, jC);
+      __syncthreads();
+      compute(kv1, bias1, jB);
+      __syncthreads();
+    }
+    // the last copy re-read a tile nobody uses: let it land before the LDS
+    // is released
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+
+  // ---- epilogue: normalise and write this lane's column ----
+  const float l_tot = lane_swap32_sum(l_part);
+  if (!row_ok) return;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (P.splits == 1) {
+    uint16_t* op = reinterpret_cast<uint16_t*>(P.out) + ((int64_t)t * P.H + hq) * kD;
+#pragma unroll
+    for (int mt = 0; mt < kD / 32; ++mt)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d0 = 32 * mt + 8 * a4 + 4 * h;
+        u32x2_t w = {pack_bf16x2(oacc[mt][4 * a4] * inv, oacc[mt][4 * a4 + 1] * inv),
+                     pack_bf16x2(oacc[mt][4 * a4 + 2] * inv, oacc[mt][4 * a4 + 3] * inv)};
+        *reinterpret_cast<u32x2_t*>(op + d0) = w;
+      }
+  } else {
+    const int64_t slotw = ((int64_t)split * P.T + t) * P.H + hq;
+    float* wo = P.ws_o + slotw * kD;
+#pragma unroll
+    for (int mt = 0; mt < kD / 32; ++mt)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d0 = 32 * mt + 8 * a4 + 4 * h;
+        *reinterpret_cast<f32x4_t*>(wo + d0) =
+            f32x4_t{oacc[mt][4 * a4] * inv, oacc[mt][4 * a4 + 1] * inv, oacc[mt][4 * a4 + 2] * inv, oacc[mt][4 * a4 + 3] * inv};
+      }
+    if (h == 0) P.ws_lse[slotw] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : kNegInf;
+  }
+}
+
+}  // namespace
+
+bool prefill_supported(const AttnParams& P, int dtype_bf16, int head_dim) {
+  // resource offsets are 32-bit: the bias rows of one wave must span less
+  // than 2 GB (E * H * (32/G + 2) entries)
+  const int64_t span = (int64_t)P.E * P.H * (32 / P.G + 2) * 2 + 256;
+  return dtype_bf16 && head_dim == kD && P.bs_log2 >= 4 && span < 0x7fffffff;
+}
+
+int launch_prefill(const AttnParams& P, hipStream_t stream) {
+  const int qtiles = (P.max_q * P.G + kRowsWG - 1) / kRowsWG;
+  dim3 grid(qtiles * P.splits, P.Hkv, P.B);
+  if (grid.x == 0 || P.B == 0) return 0;
+  hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(kWaves * 64), 0, stream, P);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace relattn
