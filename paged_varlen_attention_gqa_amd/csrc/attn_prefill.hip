@@ -10,10 +10,12 @@
 //     ahead of the arithmetic;
 //   * K rows are stored permuted inside each 32-key half: LDS row
 //     m = 8i + 4h + k holds key 16h + 4i + k, so that output register a of
-//     lane (h, n) of v_mfma_f32_32x32x16_bf16 is key 16h + a: every lane owns
-//     16 consecutive keys of its query column, and their bias values are 16
-//     consecutive entries of one rel_logits row (copied as two unaligned
-//     16-byte pieces to aligned LDS slots);
+//     lane (h, n) of v_mfma_f32_32x32x16_bf16 is key 16h + a;
+//   * the relative bias is added by the matrix cores too: two more MFMAs per
+//     32-key half multiply a constant 0 / (1/scale) selection matrix by the
+//     bias as the B operand, whose 8 k slots per lane are 8 consecutive
+//     entries of one rel_logits row (one unaligned 16-byte copy each, into
+//     aligned LDS slots), so the bias costs no vector-ALU work per score;
 //   * V^T operands come from the row-major V tile through the LDS transpose
 //     read (lane (g, i) of a 16-lane group receives V[4g + k][col0 + i]);
 //     O^T += V^T P^T takes the S^T registers as its B operand directly;
@@ -60,6 +62,22 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char* lds, ui
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds, 16, voff, 0, 0, 0);
 }
 
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding:
+// vmcnt low bits [3:0] and high bits [15:14], expcnt [6:4], lgkmcnt [11:8])
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// workgroup execution barrier without a memory fence; the empty asm keeps the
+// compiler from moving memory operations across it
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ float lane_swap32_max(float v) {
   const uint32_t u = __float_as_uint(v);
   auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
@@ -71,13 +89,18 @@ __device__ __forceinline__ float lane_swap32_sum(float v) {
   return __uint_as_float(a[0]) + __uint_as_float(a[1]);
 }
 
-__global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P) {
+// block_table is passed again as a restrict-qualified argument so that page
+// lookups compile to scalar loads (a vector load would make the next wait for
+// it also wait for the copies in flight)
+__global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
+                                                                 const int32_t* __restrict__ block_table) {
   // one LDS object per buffer, so that the compiler waits for exactly the
   // copies a read depends on
   __shared__ __attribute__((aligned(1024))) char kv0[kKV];
   __shared__ __attribute__((aligned(1024))) char kv1[kKV];
   __shared__ __attribute__((aligned(1024))) char bias0[kWaves * kBiasWave];
   __shared__ __attribute__((aligned(1024))) char bias1[kWaves * kBiasWave];
+  __shared__ __attribute__((aligned(1024))) char bias2[kWaves * kBiasWave];
 
   const int b = blockIdx.z;
   const int g = blockIdx.y;
@@ -181,17 +204,18 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P)
 
   const int bs_log2 = P.bs_log2;
   const int bs_mask = P.bs - 1;
-  const int32_t* bt_row = P.block_table + (int64_t)b * P.max_blocks;
+  const int32_t* __restrict__ bt_row = block_table + (int64_t)b * P.max_blocks;
   const int last_page = ((L > 0 ? L : 1) - 1) >> bs_log2;
   const char* kbytes = reinterpret_cast<const char*>(P.k);
   const char* vbytes = reinterpret_cast<const char*>(P.v);
   const int64_t head_bytes = (int64_t)g * kD * 2;
 
   // ---- relative-bias copy geometry ----
-  // The wave's slice of a tile: for each (half st, lane half h) the 16
-  // entries d = p - (j0 + 32st + 16h) - 15 .. +15 of each of its 32 rows,
-  // as two 8-entry pieces. LDS layout [st][h][piece][row n] x 16 bytes, so
-  // instruction q = 2st + h writes 1 KB in lane order (lane = piece*32 + n).
+  // The wave's slice of a tile: for each (half st, part u, lane half h) the
+  // 8 entries d = p - (j0 + 32st + 16u + 8h) - 7 .. +7 of each of its 32 rows,
+  // i.e. the bias of keys 32st + 16u + 8h + 7 - x for entry x. LDS layout
+  // [st][u][h][row n] x 16 bytes, so instruction q = 2st + u writes 1 KB in
+  // lane order (lane = 32h + n): each lane copies for its own column n.
   // Copies read through one resource over the wave's rows plus 64 entries
   // on each side (inside the tensor); pieces outside it read as zeros.
   const int E = P.E;
@@ -209,16 +233,41 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P)
   }
   const char* rel_base = E > 0 ? reinterpret_cast<const char*>(P.rel) + reg_lo * 2 : reinterpret_cast<const char*>(P.q);
   const __amdgpu_buffer_rsrc_t rel_rsrc = make_rsrc(rel_base, (uint32_t)((reg_hi - reg_lo) * 2));
-  // As a copy lane, lane piece*32 + n loads a piece of column n's row, with
-  // column n's position p (lanes n and n + 32 share the column). Pieces can
-  // straddle the resource only at the two ends of the whole tensor: lanes of
-  // the first or last tensor row fix their values in registers.
   const int64_t my_row_abs = (int64_t)t * P.H + hq;
   const int rel_lane_elem = (int)(my_row_abs * E - reg_lo);  // row start, relative to the resource
-  const int piece = lane >> 5;
+  // Pieces can straddle the resource only at the two ends of the whole
+  // tensor: lanes of the first or last tensor row fix their values in
+  // registers.
   const bool edge_row = E > 0 && row_ok && (my_row_abs == 0 || my_row_abs == (int64_t)P.T * P.H - 1);
+  // distances covered by a tile over the workgroup's rows: [p_lo - j0 - 63, p_hi - j0]
+  const int p_lo = ia + L - S, p_hi = ib + L - S;
+  // 0: no key of the tile gets a bias, 1: every score does, 2: some do
+  auto band_class = [&](int j0) -> int {
+    if (E == 0 || p_hi - j0 < 0 || p_lo - (j0 + kKeys - 1) >= E) return 0;
+    if (p_lo - (j0 + kKeys - 1) >= 0 && p_hi - j0 < E) return 1;
+    return 2;
+  };
+  // A operand of the bias MFMAs: lane (h', m) holds row m (key sigma(m)) and
+  // k slots 8h' + x; slot x of part u stands for key 16u + 8h' + 7 - x; the
+  // entry is 1/scale where that key is sigma(m), else 0.
+  u32x4_t bias_sel[2];
+  {
+    const int m = n;
+    const int sig = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
+    const float inv_scale = (P.scale_log2 != 0.f) ? kLog2e / P.scale_log2 : 0.f;
+    const uint32_t cbits = pack_bf16x2(inv_scale, 0.f) & 0xffffu;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int x = 16 * u + 8 * h + 7 - sig;  // slot that matches, if in 0..7
+      u32x4_t v = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (x == e) v[e >> 1] = (e & 1) ? (cbits << 16) : cbits;
+      bias_sel[u] = v;
+    }
+  }
 
-  auto issue = [&](char* kv, char* bias, int j0) {
+  auto issue_kv = [&](char* kv, int j0) {
     const int key0 = j0 + 8 * wave;
     int pidx = key0 >> bs_log2;
     pidx = pidx > last_page ? last_page : pidx;  // keys past L: any valid page of the request
@@ -232,11 +281,16 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P)
     for (int c4 = 0; c4 < 2; ++c4) dma16(kr, kv + k_dst[c4], k_src[c4]);
 #pragma unroll
     for (int c4 = 0; c4 < 2; ++c4) dma16(vr, kv + v_dst[c4], v_src[c4]);
+    asm volatile("" ::: "memory");
+  };
+  auto issue_bias = [&](char* bias, int j0) {
     char* my_bias = bias + wave * kBiasWave;
+    // a tile that no bias reaches re-reads the row's first entries (cached),
+    // so that it costs no HBM traffic
+    const bool no_bias = band_class(j0) == 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int st = q >> 1, hh = q & 1;
-      const int e_lo = p - (j0 + 32 * st + 16 * hh) - 15 + 8 * piece;
+      const int e_lo = no_bias ? 0 : p - (j0 + 16 * q + 8 * h) - 7;
       dma16(rel_rsrc, my_bias + 1024 * q, (uint32_t)(rel_lane_elem + e_lo) * 2u);
     }
     asm volatile("" ::: "memory");
@@ -249,72 +303,79 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P)
     for (int a = 0; a < 16; ++a) oacc[mt][a] = 0.f;
   float m_ref = kNegInf;  // running reference max of the column (log2 units)
   float l_part = 0.f;     // this lane's share of the column sum
-  const float scale_log2 = P.scale_log2;
+  const float scale_log2 = P.scale_log2;  // scores are acc * scale_log2 (bias included)
 
   auto compute = [&](const char* kv, const char* bias, int j0) {
-    // S^T = K Q^T for the two 32-key halves
+    // S^T = K Q^T (+ bias / scale) for the two 32-key halves
+    const int bc = band_class(j0);
+    const char* my_bias = bias + wave * kBiasWave;
     f32x16_t s[2];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int a = 0; a < 16; ++a) s[st][a] = 0.f;
+    // the two halves' MFMA chains are interleaved so that each MFMA issues
+    // while the previous one of the other chain is still in flight
 #pragma unroll
-      for (int kk = 0; kk < kD / 16; ++kk) {
+    for (int kk = 0; kk < kD / 16; ++kk)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
         const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kv + 32 * st * kRowBytes + k_rd[kk]);
         s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, kf),
                                                         __builtin_bit_cast(bf16x8v_t, qreg[kk]), s[st], 0, 0, 0);
       }
-    }
-    // bias runs: entries 0..15 of half st, from the smallest distance up
-    const char* my_bias = bias + wave * kBiasWave;
-    u32x4_t bv[2][2];
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+    for (int st = 0; st < 2; ++st) {
+      if (bc != 0) {
 #pragma unroll
-      for (int pc = 0; pc < 2; ++pc)
-        bv[st][pc] = *reinterpret_cast<const u32x4_t*>(my_bias + 1024 * (2 * st + h) + 16 * (32 * pc + n));
-    if (__builtin_amdgcn_ballot_w64(edge_row) != 0) {
-      // rows at the very start or end of the tensor: re-read their in-range
-      // entries one by one
-      if (edge_row) {
-        const uint16_t* rrow = reinterpret_cast<const uint16_t*>(P.rel) + my_row_abs * E;
+        for (int u = 0; u < 2; ++u) {
+          // entry x of this lane's piece is distance e_lo + x (key 32st + 16u + 8h + 7 - x)
+          u32x4_t bb = *reinterpret_cast<const u32x4_t*>(my_bias + 1024 * (2 * st + u) + 16 * lane);
+          const int e_lo = p - (j0 + 32 * st + 16 * u + 8 * h) - 7;
+          if (bc == 2) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-          for (int x = 0; x < 16; ++x) {
-            const int d = p - (j0 + 32 * st + 16 * h) - 15 + x;
-            if (d >= 0 && d < E) {
-              const uint32_t v = rrow[d];
-              const uint32_t w = bv[st][x >> 3][(x >> 1) & 3];
-              bv[st][x >> 3][(x >> 1) & 3] = (x & 1) ? ((w & 0xffffu) | (v << 16)) : ((w & 0xffff0000u) | v);
+            for (int w = 0; w < 4; ++w) {
+              const uint32_t lo_ok = (uint32_t)(e_lo + 2 * w) < (uint32_t)E ? 0xffffu : 0u;
+              const uint32_t hi_ok = (uint32_t)(e_lo + 2 * w + 1) < (uint32_t)E ? 0xffff0000u : 0u;
+              bb[w] &= lo_ok | hi_ok;
             }
           }
+          if (__builtin_amdgcn_ballot_w64(edge_row) != 0) {
+            // rows at the very start or end of the tensor: re-read their
+            // in-range entries one by one (clamped reads, kept where in range)
+            const uint16_t* rrow = reinterpret_cast<const uint16_t*>(P.rel) + (edge_row ? my_row_abs * E : 0);
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+              const int d = e_lo + x;
+              const bool keep = edge_row && d >= 0 && d < E;
+              const uint32_t v = rrow[keep ? d : 0];
+              const uint32_t w = bb[x >> 1];
+              const uint32_t nw = (x & 1) ? ((w & 0xffffu) | (v << 16)) : ((w & 0xffff0000u) | v);
+              bb[x >> 1] = keep ? nw : w;
+            }
+          }
+          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, bias_sel[u]),
+                                                          __builtin_bit_cast(bf16x8v_t, bb), s[st], 0, 0, 0);
+        }
       }
     }
-    // scale, bias, mask (log2 units); register a of half st is key j0 + 32st + 16h + a
+    // scale and mask (log2 units); register a of half st is key j0 + 32st + 16h + a
     const bool interior = (j0 >= lo_max) && (j0 + kKeys <= hi_min);
     float mx = kNegInf;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int jb = j0 + 32 * st + 16 * h;
-      const int dtop = p - jb;  // distance of register 0
+      // visible registers: row_lo - jb <= a < row_hi - jb
+      const int a_lo = row_lo - jb, a_hi = row_hi - jb;
 #pragma unroll
       for (int a = 0; a < 16; ++a) {
-        const int x = 15 - a;  // entry of the run
-        const uint32_t w = bv[st][x >> 3][(x >> 1) & 3];
-        const uint32_t in_range = (uint32_t)(dtop - a) < (uint32_t)E ? 0xffffffffu : 0u;
-        const float bias_v = __uint_as_float(((x & 1) ? (w & 0xffff0000u) : (w << 16)) & in_range);
-        float v = fmaf(s[st][a], scale_log2, bias_v * kLog2e);
-        if (!interior) {
-          const int j = jb + a;
-          v = (j >= row_lo && j < row_hi) ? v : kNegInf;
-        } else {
-          v = row_ok ? v : kNegInf;
-        }
+        float v = s[st][a] * scale_log2;
+        if (!interior) v = (a >= a_lo && a < a_hi) ? v : kNegInf;
         s[st][a] = v;
         mx = fmaxf(mx, v);
       }
     }
+    if (interior && !row_ok) mx = kNegInf;
     mx = lane_swap32_max(mx);
     if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleSlack) != 0) {
       const float m_new = fmaxf(m_ref, mx);
@@ -365,28 +426,48 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P)
     }
   };
 
-  // ---- key loop, double buffered: tile it+1 is copied while tile it is used ----
-  // The copies for the next tile are issued unconditionally (the last tile
-  // is re-read) so that the compiler's wait counts stay exact.
+  // ---- key loop ----
+  // K/V tiles are double buffered (copied one tile ahead), bias slices triple
+  // buffered (two tiles ahead: the bias stream has no reuse and comes from
+  // HBM). Copies past the last tile re-read it, so that every stage issues
+  // the same loads and the compiler's wait counts stay exact.
   if (tile_begin < tile_end) {
     const int last = tile_end - 1;
-    issue(kv0, bias0, kstart + kKeys * tile_begin);
-    for (int it = tile_begin; it < tile_end; it += 2) {
-      const int jA = kstart + kKeys * it;
-      const int jB = kstart + kKeys * min(it + 1, last);
-      issue(kv1, bias1, jB);
-      __syncthreads();  // buffer 0 holds tile it for every wave
-      compute(kv0, bias0, jA);
-      __syncthreads();  // everyone is done with buffer 0
+    auto j0_of = [&](int it) { return kstart + kKeys * min(it, last); };
+    issue_kv(kv0, j0_of(tile_begin));
+    issue_bias(bias0, j0_of(tile_begin));
+    issue_bias(bias1, j0_of(tile_begin + 1));
+    // One stage: copy ahead, then use tile it (K/V buffer it%2, bias it%3).
+    // The workgroup barriers carry no memory fence (a fence would wait for
+    // the copies just issued): each wave first waits for its own copies of
+    // tile it, i.e. until only the 12 copies issued after them (bias it+1,
+    // K/V it+1, bias it+2: 4 each) are outstanding, and LDS reads finish
+    // before a wave reaches the second barrier because their results are
+    // consumed by then.
+    auto stage = [&](char* kv_cur, char* b_cur, char* kv_next, char* b_next2, int it) {
+      issue_kv(kv_next, j0_of(it + 1));
+      issue_bias(b_next2, j0_of(it + 2));
+      wait_vm<12>();
+      lds_barrier();  // tile it is in LDS for every wave
+      compute(kv_cur, b_cur, j0_of(it));
+      lds_barrier();  // everyone is done with the buffers tile it+2 / it+3 will reuse
+    };
+    for (int it = tile_begin;; it += 6) {
+      stage(kv0, bias0, kv1, bias2, it);
       if (it + 1 >= tile_end) break;
-      const int jC = kstart + kKeys * min(it + 2, last);
-      issue(kv0, bias0, jC);
-      __syncthreads();
-      compute(kv1, bias1, jB);
-      __syncthreads();
+      stage(kv1, bias1, kv0, bias0, it + 1);
+      if (it + 2 >= tile_end) break;
+      stage(kv0, bias2, kv1, bias1, it + 2);
+      if (it + 3 >= tile_end) break;
+      stage(kv1, bias0, kv0, bias2, it + 3);
+      if (it + 4 >= tile_end) break;
+      stage(kv0, bias1, kv1, bias0, it + 4);
+      if (it + 5 >= tile_end) break;
+      stage(kv1, bias2, kv0, bias1, it + 5);
+      if (it + 6 >= tile_end) break;
     }
-    // the last copy re-read a tile nobody uses: let it land before the LDS
-    // is released
+    // the last copies re-read tiles nobody uses: let them land before the
+    // LDS is released
     __builtin_amdgcn_s_waitcnt(0);
   }
 
@@ -433,7 +514,7 @@ int launch_prefill(const AttnParams& P, hipStream_t stream) {
   const int qtiles = (P.max_q * P.G + kRowsWG - 1) / kRowsWG;
   dim3 grid(qtiles * P.splits, P.Hkv, P.B);
   if (grid.x == 0 || P.B == 0) return 0;
-  hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(kWaves * 64), 0, stream, P);
+  hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(kWaves * 64), 0, stream, P, P.block_table);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
