@@ -1,22 +1,31 @@
 """Benchmark: paged varlen GQA attention with the per-token relative bias on one MI355X.
 
-A step is one ``rel_attn_fwd`` call (main attention kernel, plus the split-KV
-combine kernel when the call splits) over one batch of synthetic, seeded input
-that is resident in HBM before timing starts. Default workload: batched
-decode, 64 requests x 1 query token, KV lengths uniform in [1024, 8192],
-32 query / 8 KV heads, head_dim 128, block_size 16, rel_extent 1024, bf16.
+A step is one attention call over one batch of synthetic, seeded input that
+is resident in HBM before timing starts: ``rel_attn_fwd_splits`` (the
+attention kernels) followed, when the call splits the key range, by
+``rel_attn_combine`` -- together exactly what ``rel_attn_fwd`` launches.
+Default workload: batched decode, 64 requests x 1 query token, KV lengths
+uniform in [1024, 8192], 32 query / 8 KV heads, head_dim 128, block_size 16,
+rel_extent 1024, bf16.
 
 Prints ONE JSON line. ``value`` is the algorithmic bytes of a step (K/V rows
 of visible keys, in-range bias, q, out, page-table entries) divided by the
-measured step time. ``roofline`` compares the same figure (or TFLOP/s for a
-compute-bound workload) with MI355X's published peak, using per-call HIP
-event timings taken on the stream the kernels run on. ``cpu_baseline`` times
-the fp64 CPU oracle on a bounded sample of the same workload.
+wall-clock step time. ``roofline`` divides the same algorithmic figure (or
+the flops, for the compute-bound prefill workload) by the attention stage's
+own average duration, from HIP events recorded around it on the stream its
+kernels run on, and compares that with MI355X's published peak. Its
+``traffic`` is the HBM-side bytes per launch measured by rocprofv3 counters
+(FETCH_SIZE, WRITE_SIZE, scaled by the same counters' reading for a plain copy
+of known size), read from the committed counter summary under profiles/ when
+that summary was taken on the current kernel sources, else null.
+``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same
+workload.
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -29,7 +38,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-from paged_varlen_attention_gqa_amd import rel_attn_fwd, rel_attn_num_splits, rel_attn_workspace_bytes  # noqa: E402
+from paged_varlen_attention_gqa_amd import (rel_attn_combine, rel_attn_fwd_splits,  # noqa: E402
+                                           rel_attn_num_splits, rel_attn_workspace_bytes)
 from paged_varlen_attention_gqa_amd.inputs import config_spec, make_case  # noqa: E402
 from paged_varlen_attention_gqa_amd.work import case_work  # noqa: E402
 
@@ -54,13 +64,69 @@ BOUND = {"decode_b64": "hbm", "decode_long_b1": "hbm", "mixed_window": "hbm",
          "prefill_chunked": "mfma", "tiny_fp32": "hbm"}
 
 
+# Kernel sources whose code decides the attention stage's memory traffic, per
+# workload; a counter summary is valid only for the sources it was taken on.
+CSRC = os.path.join(ROOT, "paged_varlen_attention_gqa_amd", "csrc")
+STAGE_SOURCES = {
+    "decode_b64": ["attn_decode.hip"],
+    "decode_long_b1": ["attn_decode.hip"],
+    "prefill_chunked": ["attn_decode.hip", "attn_prefill.hip"],
+    "mixed_window": ["attn_decode.hip", "attn_prefill.hip"],
+    "tiny_fp32": ["attn_general.hip"],
+}
+STAGE_KERNELS = {
+    "decode_b64": "attn_decode_kernel",
+    "decode_long_b1": "attn_decode_kernel",
+    "prefill_chunked": "attn_decode_kernel (no work: rows > 16) + attn_prefill_kernel",
+    "mixed_window": "attn_decode_kernel + attn_prefill_kernel",
+    "tiny_fp32": "attn_general_kernel",
+}
+COPY_BYTES = 2 << 30  # the plain copy that calibrates the HBM counters
+
+
+def sources_digest(name: str) -> str:
+    h = hashlib.sha256()
+    for f in STAGE_SOURCES[name] + ["device_common.h", "api.cpp"]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(name: str):
+    """HBM bytes per launch of the attention stage from profiles/hbm_traffic_<name>.txt
+    (``key: value`` lines), or None when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{name}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith((" ", "#")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_sources_sha256") != sources_digest(name):
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def _log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
 def cpu_baseline(case, name: str, budget_s: float = 20.0) -> dict:
     """Time the fp64 oracle on a bounded sample of the same workload (whole requests
-    for decode workloads, a token sample otherwise); scaled to GB/s or TFLOP/s."""
+    for decode workloads, a token sample otherwise); scaled to GB/s or TFLOP/s.
+    The oracle runs on one thread (its BLAS pool limited to 1), so ``cores`` is 1."""
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(limits=1):
+        return _cpu_baseline(case, name, budget_s)
+
+
+def _cpu_baseline(case, name: str, budget_s: float) -> dict:
     import oracle
     from paged_varlen_attention_gqa_amd.work import count_work
 
@@ -87,7 +153,7 @@ def cpu_baseline(case, name: str, budget_s: float = 20.0) -> dict:
                    num_heads=case.num_heads, num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
                    block_size=case.block_size, rel_extent=case.rel_extent, causal=case.causal,
                    window_size=case.window_size, elem_bytes=elem)
-    cores = len(os.sched_getaffinity(0))
+    cores = 1
     if bound == "mfma":
         value, unit = w.flops / t_total / 1e12, "TFLOP/s"
     else:
@@ -108,6 +174,8 @@ def main():
     ap.add_argument("--config", default="decode_b64", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--num-splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 2 GiB copy first (for HBM counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this path has no "
@@ -131,8 +199,26 @@ def main():
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        rel_attn_fwd(**kw, num_splits=splits, out=out, workspace=ws)
+    if args.copy_calibration:
+        # a plain copy of known size, for scaling the HBM counters of a
+        # profiling run (2 GiB read + 2 GiB written, far beyond the caches)
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        _log(f"[bench] copy calibration: {COPY_BYTES} bytes read + written, 3 times")
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        rel_attn_fwd_splits(**kw, num_splits=splits, out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        if splits > 1:
+            rel_attn_combine(ws, out, splits)
 
     _log(f"[bench] warmup {args.warmup} (num_splits={splits})")
     for _ in range(args.warmup):
@@ -143,28 +229,27 @@ def main():
     _log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e0, e1 in evs:
-        e0.record(stream)
-        step()
-        e1.record(stream)
+    for ev in evs:
+        step(ev)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    call_ms = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    stage_ms = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
     ms_per_step = wall * 1e3 / args.steps
     gbs = work.bytes / (ms_per_step * 1e-3) / 1e9
     tflops = work.flops / (ms_per_step * 1e-3) / 1e12
-    avg_call_s = float(call_ms.mean()) * 1e-3
+    avg_call_s = float(stage_ms.mean()) * 1e-3
+    traffic = measured_traffic(name)
     bound = BOUND[name]
     if bound == "mfma":
         peak = BF16_MFMA_PEAK_TFLOPS if case.dtype == torch.bfloat16 else FP32_MFMA_PEAK_TFLOPS
         ach = work.flops / avg_call_s / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 3), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4), "traffic": None}
+                "frac": round(ach / peak, 4), "traffic": traffic}
         value, unit = tflops, "TFLOP/s"
     else:
         ach = work.bytes / avg_call_s / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
         value, unit = gbs, "GB/s"
     res = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
@@ -173,8 +258,9 @@ def main():
         "dtype": "bf16" if case.dtype == torch.bfloat16 else "f32", "data": "synthetic",
         "config": {"workload": f"{name}: {DESCRIPTIONS[name]}", "num_splits": splits,
                    "algorithmic_bytes": work.bytes, "algorithmic_flops": work.flops,
-                   "call_us_mean": round(float(call_ms.mean()) * 1e3, 2),
-                   "call_us_min": round(float(call_ms.min()) * 1e3, 2),
+                   "stage_kernels": STAGE_KERNELS[name],
+                   "stage_us_mean": round(float(stage_ms.mean()) * 1e3, 2),
+                   "stage_us_min": round(float(stage_ms.min()) * 1e3, 2),
                    "tflops": round(tflops, 3), "gbs": round(gbs, 2)},
         "roofline": roof,
     }

@@ -124,6 +124,9 @@ size_t rel_attn_workspace_bytes(int num_splits, int num_tokens, int num_heads, i
  * into range, and a request with L_b < S_b yields zeros for the rows whose
  * position is negative.
  * Returns REL_ATTN_OK, or one of the negative codes above.
+ *
+ * It is rel_attn_fwd_splits followed, when num_splits > 1, by
+ * rel_attn_combine on the same stream.
  */
 int rel_attn_fwd(const void* q, const void* key_cache, const void* value_cache,
                  const int32_t* block_table, const int32_t* cache_seqlens,
@@ -133,6 +136,50 @@ int rel_attn_fwd(const void* q, const void* key_cache, const void* value_cache,
                  int rel_extent, float softmax_scale, int causal, int window_left,
                  int window_right, int num_splits, void* workspace, size_t workspace_bytes,
                  size_t* workspace_needed, void* stream);
+
+/*
+ * rel_attn_fwd_splits - the attention stage of rel_attn_fwd alone: same
+ * arguments, same checks, same return codes.
+ *
+ * With num_splits == 1 it is rel_attn_fwd (the result goes to `out`). With
+ * num_splits > 1 it leaves `out` untouched and writes, for every split k,
+ * token t and head h, the normalised partial output over the keys of split k
+ * and its log-sum-exp into the workspace, laid out as
+ *   float o[num_splits][num_tokens][num_heads][head_dim], followed by
+ *   float lse[num_splits][num_tokens][num_heads]
+ * where lse is the natural-log log-sum-exp of the scores (softmax_scale * q.k
+ * + bias) of the split's visible keys, -inf for a split with none (its o is
+ * then zero). Every entry is written. rel_attn_combine then produces `out`.
+ * This is the split-KV scheme behind the num_splits argument of the
+ * docs.vllm.ai `inkling_fa4_rel_attention` / `inkling_fa4_num_splits` pages.
+ */
+int rel_attn_fwd_splits(const void* q, const void* key_cache, const void* value_cache,
+                        const int32_t* block_table, const int32_t* cache_seqlens,
+                        const int32_t* cu_seqlens_q, const void* rel_logits, void* out, int dtype,
+                        int num_tokens, int batch_size, int max_seqlen_q, int max_blocks_per_seq,
+                        int num_heads, int num_kv_heads, int head_dim, int num_blocks,
+                        int block_size, int rel_extent, float softmax_scale, int causal,
+                        int window_left, int window_right, int num_splits, void* workspace,
+                        size_t workspace_bytes, size_t* workspace_needed, void* stream);
+
+/*
+ * rel_attn_combine - merge the per-split partial results that
+ * rel_attn_fwd_splits left in `workspace` (layout above) into `out`
+ * [num_tokens][num_heads][head_dim] of type dtype:
+ *   out = sum_k exp(lse_k - LSE) * o_k,  LSE = log sum_k exp(lse_k),
+ * zeros where every lse_k is -inf.
+ *
+ * workspace: device memory, >= rel_attn_workspace_bytes(num_splits, ...)
+ *            bytes, 16-byte aligned, read only.
+ * num_splits: 2..128 (with one split there is nothing to merge).
+ * head_dim:  64 or 128. stream: hipStream_t (NULL = default stream).
+ * Returns REL_ATTN_OK, REL_ATTN_EINVAL (bad size, NULL out with
+ * num_tokens > 0, misaligned workspace), REL_ATTN_EUNSUPPORTED (dtype,
+ * head_dim), REL_ATTN_EWORKSPACE (workspace NULL or too small) or
+ * REL_ATTN_ELAUNCH. Asynchronous; allocates nothing.
+ */
+int rel_attn_combine(const void* workspace, size_t workspace_bytes, void* out, int dtype,
+                     int num_tokens, int num_heads, int head_dim, int num_splits, void* stream);
 
 /* rel_attn_strerror - static description of a return code (never NULL). */
 const char* rel_attn_strerror(int code);

@@ -10,8 +10,11 @@ of a call.
 from .relattn import (  # noqa: F401
     RelAttnError,
     load_library,
+    rel_attn_combine,
     rel_attn_fwd,
+    rel_attn_fwd_splits,
     rel_attn_num_splits,
     rel_attn_strerror,
     rel_attn_workspace_bytes,
+    split_partials,
 )

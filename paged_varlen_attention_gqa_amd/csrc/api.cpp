@@ -70,15 +70,20 @@ extern "C" const char* rel_attn_strerror(int code) {
   }
 }
 
-extern "C" int rel_attn_fwd(const void* q, const void* key_cache, const void* value_cache,
-                            const int32_t* block_table, const int32_t* cache_seqlens,
-                            const int32_t* cu_seqlens_q, const void* rel_logits, void* out, int dtype,
-                            int num_tokens, int batch_size, int max_seqlen_q, int max_blocks_per_seq,
-                            int num_heads, int num_kv_heads, int head_dim, int num_blocks, int block_size,
-                            int rel_extent, float softmax_scale, int causal, int window_left,
-                            int window_right, int num_splits, void* workspace, size_t workspace_bytes,
-                            size_t* workspace_needed, void* stream) {
-  // ---- argument checks (host only, before any launch) ----
+namespace {
+
+// Host-side checks and parameter set-up shared by rel_attn_fwd and
+// rel_attn_fwd_splits. Returns REL_ATTN_OK with *launch = true when kernels
+// must run, REL_ATTN_OK with *launch = false for a workspace query or an empty
+// call, or a negative code.
+int prepare(const void* q, const void* key_cache, const void* value_cache, const int32_t* block_table,
+            const int32_t* cache_seqlens, const int32_t* cu_seqlens_q, const void* rel_logits, void* out,
+            int dtype, int num_tokens, int batch_size, int max_seqlen_q, int max_blocks_per_seq,
+            int num_heads, int num_kv_heads, int head_dim, int num_blocks, int block_size, int rel_extent,
+            float softmax_scale, int causal, int window_left, int window_right, int num_splits,
+            void* workspace, size_t workspace_bytes, size_t* workspace_needed, AttnParams* P_out,
+            bool* launch) {
+  *launch = false;
   if (num_tokens < 0 || batch_size < 0 || max_seqlen_q < 0 || max_blocks_per_seq < 0 || num_heads < 1 ||
       num_kv_heads < 1 || head_dim < 1 || num_blocks < 0 || block_size < 1 || rel_extent < 0 ||
       window_left < -1 || window_right < -1 || (causal != 0 && causal != 1))
@@ -109,7 +114,8 @@ extern "C" int rel_attn_fwd(const void* q, const void* key_cache, const void* va
   }
   if (num_tokens == 0 || batch_size == 0 || max_seqlen_q == 0) return REL_ATTN_OK;
 
-  AttnParams P{};
+  AttnParams& P = *P_out;
+  P = AttnParams{};
   P.q = q;
   P.k = key_cache;
   P.v = value_cache;
@@ -158,14 +164,19 @@ extern "C" int rel_attn_fwd(const void* q, const void* key_cache, const void* va
     if (chunk < 16) chunk = 16;
     P.dec_chunk = chunk > (1 << 30) ? (1 << 30) : (int)chunk;
   }
+  *launch = true;
+  return REL_ATTN_OK;
+}
 
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+// The attention kernels of one call: partials into the workspace when the
+// call splits, else the final output.
+int launch_attention(AttnParams& P, int dtype, int head_dim, hipStream_t s) {
   const int bf16 = dtype == REL_ATTN_BF16;
   if (relattn::decode_supported(P, bf16, head_dim)) {
     if (relattn::launch_decode(P, head_dim, s) != 0) return REL_ATTN_ELAUNCH;
-    // requests with more than 16 packed rows go to the general kernel
+    // requests with more than 16 packed rows go to the prefill kernel
     P.mode = 1;
-    if ((int64_t)max_seqlen_q * G > relattn::kDecodeMaxRows) {
+    if ((int64_t)P.max_q * P.G > relattn::kDecodeMaxRows) {
       const int rc = relattn::prefill_supported(P, bf16, head_dim) ? relattn::launch_prefill(P, s)
                                                                    : relattn::launch_general(P, bf16, head_dim, s);
       if (rc != 0) return REL_ATTN_ELAUNCH;
@@ -174,6 +185,75 @@ extern "C" int rel_attn_fwd(const void* q, const void* key_cache, const void* va
     P.mode = 0;
     if (relattn::launch_general(P, bf16, head_dim, s) != 0) return REL_ATTN_ELAUNCH;
   }
-  if (num_splits > 1 && relattn::launch_combine(P, bf16, head_dim, s) != 0) return REL_ATTN_ELAUNCH;
   return REL_ATTN_OK;
+}
+
+}  // namespace
+
+#define REL_ATTN_ARGS                                                                                    \
+  q, key_cache, value_cache, block_table, cache_seqlens, cu_seqlens_q, rel_logits, out, dtype,         \
+      num_tokens, batch_size, max_seqlen_q, max_blocks_per_seq, num_heads, num_kv_heads, head_dim,     \
+      num_blocks, block_size, rel_extent, softmax_scale, causal, window_left, window_right, num_splits, \
+      workspace, workspace_bytes, workspace_needed
+
+extern "C" int rel_attn_fwd(const void* q, const void* key_cache, const void* value_cache,
+                            const int32_t* block_table, const int32_t* cache_seqlens,
+                            const int32_t* cu_seqlens_q, const void* rel_logits, void* out, int dtype,
+                            int num_tokens, int batch_size, int max_seqlen_q, int max_blocks_per_seq,
+                            int num_heads, int num_kv_heads, int head_dim, int num_blocks, int block_size,
+                            int rel_extent, float softmax_scale, int causal, int window_left,
+                            int window_right, int num_splits, void* workspace, size_t workspace_bytes,
+                            size_t* workspace_needed, void* stream) {
+  AttnParams P;
+  bool launch = false;
+  int rc = prepare(REL_ATTN_ARGS, &P, &launch);
+  if (rc != REL_ATTN_OK || !launch) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  rc = launch_attention(P, dtype, head_dim, s);
+  if (rc != REL_ATTN_OK) return rc;
+  if (num_splits > 1 && relattn::launch_combine(P, dtype == REL_ATTN_BF16, head_dim, s) != 0)
+    return REL_ATTN_ELAUNCH;
+  return REL_ATTN_OK;
+}
+
+extern "C" int rel_attn_fwd_splits(const void* q, const void* key_cache, const void* value_cache,
+                                   const int32_t* block_table, const int32_t* cache_seqlens,
+                                   const int32_t* cu_seqlens_q, const void* rel_logits, void* out,
+                                   int dtype, int num_tokens, int batch_size, int max_seqlen_q,
+                                   int max_blocks_per_seq, int num_heads, int num_kv_heads, int head_dim,
+                                   int num_blocks, int block_size, int rel_extent, float softmax_scale,
+                                   int causal, int window_left, int window_right, int num_splits,
+                                   void* workspace, size_t workspace_bytes, size_t* workspace_needed,
+                                   void* stream) {
+  AttnParams P;
+  bool launch = false;
+  int rc = prepare(REL_ATTN_ARGS, &P, &launch);
+  if (rc != REL_ATTN_OK || !launch) return rc;
+  return launch_attention(P, dtype, head_dim, reinterpret_cast<hipStream_t>(stream));
+}
+
+#undef REL_ATTN_ARGS
+
+extern "C" int rel_attn_combine(const void* workspace, size_t workspace_bytes, void* out, int dtype,
+                                int num_tokens, int num_heads, int head_dim, int num_splits,
+                                void* stream) {
+  if (num_tokens < 0 || num_heads < 1 || num_splits < 2 || num_splits > kMaxSplits)
+    return REL_ATTN_EINVAL;
+  if (dtype != REL_ATTN_FP32 && dtype != REL_ATTN_BF16) return REL_ATTN_EUNSUPPORTED;
+  if (!supported_head_dim(head_dim)) return REL_ATTN_EUNSUPPORTED;
+  const size_t need = rel_attn_workspace_bytes(num_splits, num_tokens, num_heads, head_dim);
+  if (workspace == nullptr || workspace_bytes < need) return REL_ATTN_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return REL_ATTN_EINVAL;
+  if (num_tokens == 0) return REL_ATTN_OK;
+  if (out == nullptr) return REL_ATTN_EINVAL;
+  AttnParams P{};
+  P.out = out;
+  P.ws_o = reinterpret_cast<float*>(const_cast<void*>(workspace));
+  P.ws_lse = P.ws_o + (size_t)num_splits * num_tokens * num_heads * head_dim;
+  P.T = num_tokens;
+  P.H = num_heads;
+  P.splits = num_splits;
+  return relattn::launch_combine(P, dtype == REL_ATTN_BF16, head_dim, reinterpret_cast<hipStream_t>(stream)) == 0
+             ? REL_ATTN_OK
+             : REL_ATTN_ELAUNCH;
 }

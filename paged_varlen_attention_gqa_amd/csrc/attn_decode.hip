@@ -128,9 +128,22 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams P) {
   const int ntiles = __builtin_amdgcn_readfirstlane(c1 > c0 ? (c1 - c0 + kTile - 1) / kTile : 0);
 
   if (ntiles == 0) {
-    // an empty split still tells the combine step it holds nothing
-    if (P.splits > 1 && wave == 0 && q == 0 && col_ok)
-      P.ws_lse[((int64_t)split * P.T + t) * P.H + h] = kNegInf;
+    // No visible key: the row's output is zero, and an empty split still
+    // tells the combine step that it holds nothing. Lane (n, q) of wave 0
+    // writes dims 32q .. 32q+31 of column n.
+    if (wave == 0 && col_ok) {
+      if (P.splits == 1) {
+        uint16_t* op = reinterpret_cast<uint16_t*>(P.out) + ((int64_t)t * P.H + h) * kD + 32 * q;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(op + 8 * i) = u32x4_t{0u, 0u, 0u, 0u};
+      } else {
+        const int64_t slot = ((int64_t)split * P.T + t) * P.H + h;
+        float* wo = P.ws_o + slot * kD + 32 * q;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) *reinterpret_cast<f32x4_t*>(wo + 4 * i) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (q == 0) P.ws_lse[slot] = kNegInf;
+      }
+    }
     return;
   }
 

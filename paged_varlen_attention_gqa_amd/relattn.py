@@ -55,6 +55,10 @@ def load_library() -> ctypes.CDLL:
         + [c_vp, c_size, ctypes.POINTER(c_size), c_vp]
     )
     lib.rel_attn_fwd.restype = c_int
+    lib.rel_attn_fwd_splits.argtypes = lib.rel_attn_fwd.argtypes
+    lib.rel_attn_fwd_splits.restype = c_int
+    lib.rel_attn_combine.argtypes = [c_vp, c_size, c_vp] + [c_int] * 5 + [c_vp]
+    lib.rel_attn_combine.restype = c_int
     _lib = lib
     return lib
 
@@ -93,18 +97,9 @@ def _check_dev(name, t, dtype=None):
         raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
 
 
-def rel_attn_fwd(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor, *,
-                 block_table: torch.Tensor, cache_seqlens: torch.Tensor, cu_seqlens_q: torch.Tensor,
-                 max_seqlen_q: int, softmax_scale: float, causal: bool, window_size=(-1, -1),
-                 rel_extent: int, rel_logits: torch.Tensor | None, num_splits: int | None = None,
-                 out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                 max_kv_len: int | None = None) -> torch.Tensor:
-    """Paged varlen GQA attention with the per-token relative bias; returns ``out``.
-
-    ``num_splits=None`` asks :func:`rel_attn_num_splits`, with ``max_kv_len``
-    defaulting to the page-table capacity (``block_table.shape[1] *
-    block_size``), so no device value is read on the host.
-    """
+def _attention_call(entry: str, q, key_cache, value_cache, *, block_table, cache_seqlens,
+                    cu_seqlens_q, max_seqlen_q, softmax_scale, causal, window_size, rel_extent,
+                    rel_logits, num_splits, out, workspace, max_kv_len):
     lib = load_library()
     if q.dtype == torch.bfloat16:
         dt = BF16
@@ -148,7 +143,7 @@ def rel_attn_fwd(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Te
             _check_dev("workspace", workspace)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    rc = lib.rel_attn_fwd(
+    rc = getattr(lib, entry)(
         _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(block_table), _ptr(cache_seqlens),
         _ptr(cu_seqlens_q), _ptr(rel_logits if rel_extent > 0 else None), _ptr(out),
         dt, T, B, int(max_seqlen_q), block_table.shape[1], H, HKV, D, NB, BS, int(rel_extent),
@@ -156,5 +151,77 @@ def rel_attn_fwd(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Te
         _ptr(workspace) if need > 0 else ctypes.c_void_p(0), ws_bytes, None,
         ctypes.c_void_p(stream))
     if rc != 0:
-        raise RelAttnError(f"rel_attn_fwd: {rel_attn_strerror(rc)} (code {rc})")
+        raise RelAttnError(f"{entry}: {rel_attn_strerror(rc)} (code {rc})")
+    return out, workspace, num_splits
+
+
+def rel_attn_fwd(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor, *,
+                 block_table: torch.Tensor, cache_seqlens: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                 max_seqlen_q: int, softmax_scale: float, causal: bool, window_size=(-1, -1),
+                 rel_extent: int, rel_logits: torch.Tensor | None, num_splits: int | None = None,
+                 out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                 max_kv_len: int | None = None) -> torch.Tensor:
+    """Paged varlen GQA attention with the per-token relative bias; returns ``out``.
+
+    ``num_splits=None`` asks :func:`rel_attn_num_splits`, with ``max_kv_len``
+    defaulting to the page-table capacity (``block_table.shape[1] *
+    block_size``), so no device value is read on the host.
+    """
+    out, _, _ = _attention_call(
+        "rel_attn_fwd", q, key_cache, value_cache, block_table=block_table,
+        cache_seqlens=cache_seqlens, cu_seqlens_q=cu_seqlens_q, max_seqlen_q=max_seqlen_q,
+        softmax_scale=softmax_scale, causal=causal, window_size=window_size, rel_extent=rel_extent,
+        rel_logits=rel_logits, num_splits=num_splits, out=out, workspace=workspace,
+        max_kv_len=max_kv_len)
+    return out
+
+
+def rel_attn_fwd_splits(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor, *,
+                        block_table: torch.Tensor, cache_seqlens: torch.Tensor,
+                        cu_seqlens_q: torch.Tensor, max_seqlen_q: int, softmax_scale: float,
+                        causal: bool, window_size=(-1, -1), rel_extent: int,
+                        rel_logits: torch.Tensor | None, num_splits: int | None = None,
+                        out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                        max_kv_len: int | None = None):
+    """The attention stage alone; returns ``(out, workspace, num_splits)``.
+
+    With one split ``out`` holds the result. With more, ``out`` is untouched
+    and ``workspace`` holds the per-split partial outputs and log-sum-exps
+    (layout in include/rel_attn.h); :func:`rel_attn_combine` merges them.
+    """
+    return _attention_call(
+        "rel_attn_fwd_splits", q, key_cache, value_cache, block_table=block_table,
+        cache_seqlens=cache_seqlens, cu_seqlens_q=cu_seqlens_q, max_seqlen_q=max_seqlen_q,
+        softmax_scale=softmax_scale, causal=causal, window_size=window_size, rel_extent=rel_extent,
+        rel_logits=rel_logits, num_splits=num_splits, out=out, workspace=workspace,
+        max_kv_len=max_kv_len)
+
+
+def split_partials(workspace: torch.Tensor, num_splits: int, num_tokens: int, num_heads: int,
+                   head_dim: int):
+    """Views ``(o [splits, T, H, D], lse [splits, T, H])`` of a split workspace (fp32)."""
+    n_o = num_splits * num_tokens * num_heads * head_dim
+    f = workspace.view(torch.float32)
+    o = f[:n_o].view(num_splits, num_tokens, num_heads, head_dim)
+    lse = f[n_o:n_o + num_splits * num_tokens * num_heads].view(num_splits, num_tokens, num_heads)
+    return o, lse
+
+
+def rel_attn_combine(workspace: torch.Tensor, out: torch.Tensor, num_splits: int) -> torch.Tensor:
+    """Merge the partials of :func:`rel_attn_fwd_splits` into ``out`` [T, H, D]; returns ``out``."""
+    lib = load_library()
+    _check_dev("workspace", workspace)
+    _check_dev("out", out)
+    if out.dtype == torch.bfloat16:
+        dt = BF16
+    elif out.dtype == torch.float32:
+        dt = FP32
+    else:
+        raise ValueError(f"unsupported dtype {out.dtype}")
+    T, H, D = out.shape
+    stream = torch.cuda.current_stream(out.device).cuda_stream
+    rc = lib.rel_attn_combine(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _ptr(out), dt, T, H, D, int(num_splits), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise RelAttnError(f"rel_attn_combine: {rel_attn_strerror(rc)} (code {rc})")
     return out

@@ -32,8 +32,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert set(names) >= {"rel_attn_fwd", "rel_attn_num_splits", "rel_attn_workspace_bytes",
-                          "rel_attn_strerror"}
+    assert set(names) >= {"rel_attn_fwd", "rel_attn_fwd_splits", "rel_attn_combine",
+                          "rel_attn_num_splits", "rel_attn_workspace_bytes", "rel_attn_strerror"}
     for n in names:
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -69,14 +69,14 @@ def test_workspace_bytes(lib):
     assert lib.rel_attn_workspace_bytes(0, 64, 32, 128) == 0
 
 
-def _fwd(lib, **over):
+def _fwd(lib, entry="rel_attn_fwd", **over):
     a = dict(q=1, k=1, v=1, bt=1, sl=1, cu=1, rel=1, out=1, dtype=1, T=4, B=2, maxq=2, mb=3, H=8,
              Hkv=2, D=128, NB=10, bs=16, E=4, scale=0.1, causal=1, wl=-1, wr=-1, splits=1, ws=None,
              wsb=0, need=None, stream=None)
     a.update(over)
     ptr = lambda x: ctypes.c_void_p(x) if x else ctypes.c_void_p(0)  # noqa: E731
     need = a["need"]
-    return lib.rel_attn_fwd(
+    return getattr(lib, entry)(
         ptr(a["q"]), ptr(a["k"]), ptr(a["v"]), ptr(a["bt"]), ptr(a["sl"]), ptr(a["cu"]), ptr(a["rel"]),
         ptr(a["out"]), a["dtype"], a["T"], a["B"], a["maxq"], a["mb"], a["H"], a["Hkv"], a["D"], a["NB"],
         a["bs"], a["E"], a["scale"], a["causal"], a["wl"], a["wr"], a["splits"], ptr(a["ws"]), a["wsb"],
@@ -101,15 +101,43 @@ def _fwd(lib, **over):
     (dict(splits=4, ws=16, wsb=100), -3),
     (dict(splits=4, ws=17, wsb=1 << 30), -1),  # misaligned workspace
 ])
-def test_fwd_rejects_before_launch(lib, over, code):
-    assert _fwd(lib, **over) == code
+@pytest.mark.parametrize("entry", ["rel_attn_fwd", "rel_attn_fwd_splits"])
+def test_fwd_rejects_before_launch(lib, entry, over, code):
+    assert _fwd(lib, entry, **over) == code
 
 
-def test_fwd_workspace_query(lib):
+@pytest.mark.parametrize("entry", ["rel_attn_fwd", "rel_attn_fwd_splits"])
+def test_fwd_workspace_query(lib, entry):
     need = ctypes.c_size_t(123)
-    assert _fwd(lib, splits=8, need=need) == 0
+    assert _fwd(lib, entry, splits=8, need=need) == 0
     assert need.value == 8 * 4 * 8 * 129 * 4
 
 
-def test_fwd_empty_call_is_ok(lib):
-    assert _fwd(lib, T=0, B=0, q=0, out=0) == 0
+@pytest.mark.parametrize("entry", ["rel_attn_fwd", "rel_attn_fwd_splits"])
+def test_fwd_empty_call_is_ok(lib, entry):
+    assert _fwd(lib, entry, T=0, B=0, q=0, out=0) == 0
+
+
+def _combine(lib, ws=16, wsb=1 << 30, out=16, dtype=1, T=4, H=8, D=128, splits=4):
+    p = lambda x: ctypes.c_void_p(x) if x else ctypes.c_void_p(0)  # noqa: E731
+    return lib.rel_attn_combine(p(ws), wsb, p(out), dtype, T, H, D, splits, None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(splits=1), -1),         # nothing to merge
+    (dict(splits=129), -1),
+    (dict(T=-1), -1),
+    (dict(H=0), -1),
+    (dict(out=0), -1),
+    (dict(ws=17), -1),            # misaligned workspace
+    (dict(dtype=5), -2),
+    (dict(D=80), -2),
+    (dict(ws=0), -3),
+    (dict(wsb=4 * 4 * 8 * 129 * 4 - 1), -3),
+])
+def test_combine_rejects_before_launch(lib, over, code):
+    assert _combine(lib, **over) == code
+
+
+def test_combine_empty_call_is_ok(lib):
+    assert _combine(lib, T=0, out=0) == 0

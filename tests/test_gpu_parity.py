@@ -176,3 +176,26 @@ def test_preallocated_out_and_determinism():
     r2 = rel_attn_fwd(**kw)
     torch.cuda.synchronize()
     assert torch.equal(r, r2)
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_requests_without_keys_give_zeros(splits, dtype):
+    """Requests whose cache length is 0 (one decode query, a 20-query chunk)
+    see no key: their rows are zeros, written over a NaN-filled output."""
+    case = make_case(name="no_keys", query_lens=[1, 20, 1, 3], kv_lens=[40, 20, 300, 50],
+                     num_heads=8, num_kv_heads=2, head_dim=128, block_size=16, rel_extent=16,
+                     dtype=dtype)
+    lens = torch.tensor([0, 0, 300, 50], dtype=torch.int32)
+    kw = device_case(case)
+    kw["cache_seqlens"] = lens.cuda()
+    from paged_varlen_attention_gqa_amd import rel_attn_fwd
+
+    out = torch.full_like(kw["q"], float("nan"))
+    rel_attn_fwd(**kw, num_splits=splits, out=out)
+    torch.cuda.synchronize()
+    ref_kw = case.kwargs()
+    ref_kw["cache_seqlens"] = lens
+    ref = oracle.oracle_attention(**ref_kw)
+    compare(out, ref, case.dtype, what=f"no keys splits={splits}")
+    assert torch.count_nonzero(out[:21]) == 0

@@ -1,0 +1,95 @@
+"""The two-stage path: rel_attn_fwd_splits (per-split partial outputs and
+log-sum-exps) followed by rel_attn_combine.
+
+Checked against the fp64 oracle: the log-sum-exp over the splits of each row
+must equal the row's full log-sum-exp, and the combined output must equal
+both the oracle's output (at the parity tolerance) and rel_attn_fwd's output
+bit for bit (the one-call entry point launches the same kernels). The
+workspace is filled with NaN first, so an entry left unwritten shows up.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import compare, device_case, log
+from paged_varlen_attention_gqa_amd import (rel_attn_combine, rel_attn_fwd, rel_attn_fwd_splits,
+                                           rel_attn_workspace_bytes, split_partials)
+from paged_varlen_attention_gqa_amd.inputs import make_case, make_config
+
+pytestmark = pytest.mark.gpu
+
+# log-sum-exp of a row, natural log: bf16 inputs are exact in the fp32 score
+# arithmetic, so the error is fp32 accumulation plus the exponent evaluation.
+LSE_TOL = {torch.bfloat16: 1e-2, torch.float32: 1e-4}
+
+
+def _two_stage(case, splits):
+    kw = device_case(case)
+    T, H, D = case.num_tokens, case.num_heads, case.head_dim
+    need = rel_attn_workspace_bytes(splits, T, H, D)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ws.view(torch.float32).fill_(float("nan"))
+    sentinel = torch.full_like(kw["q"], 3.0)
+    out, ws, n = rel_attn_fwd_splits(**kw, num_splits=splits, out=sentinel.clone(), workspace=ws)
+    torch.cuda.synchronize()
+    assert n == splits
+    assert torch.equal(out, sentinel), "the split stage must leave out untouched"
+    o, lse = split_partials(ws, splits, T, H, D)
+    o64 = o.cpu().double().numpy()
+    lse64 = lse.cpu().double().numpy()
+    assert not np.isnan(o64).any() and not np.isnan(lse64).any(), "unwritten workspace entries"
+    assert np.all(np.isfinite(o64))
+    assert not np.isposinf(lse64).any()
+    comb = rel_attn_combine(ws, torch.empty_like(kw["q"]), splits)
+    one = rel_attn_fwd(**kw, num_splits=splits)
+    torch.cuda.synchronize()
+    return o64, lse64, comb, one
+
+
+CASES = [
+    ("decode_b64@1/16", lambda: make_config("decode_b64", scale=1 / 16), 8),
+    ("decode_long_b1@1/16", lambda: make_config("decode_long_b1", scale=1 / 16), 16),
+    ("prefill_chunked@1/8", lambda: make_config("prefill_chunked", scale=1 / 8), 3),
+    ("fp32_general", lambda: make_case(name="fp32_splits", query_lens=[3, 1, 9], kv_lens=[300, 41, 90],
+                                       num_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+                                       rel_extent=50, dtype=torch.float32), 5),
+    ("empty_splits", lambda: make_case(name="empty_splits", query_lens=[1, 2], kv_lens=[20, 3000],
+                                       num_heads=16, num_kv_heads=4, head_dim=128, block_size=16,
+                                       rel_extent=64), 64),
+]
+
+
+@pytest.mark.parametrize("name,mk,splits", CASES, ids=[c[0] for c in CASES])
+def test_split_stage_then_combine(name, mk, splits):
+    case = mk()
+    log(f"[splits] {name}: T={case.num_tokens} H={case.num_heads} splits={splits}")
+    o64, lse64, comb, one = _two_stage(case, splits)
+    ref, ref_lse = oracle.oracle_attention(**case.kwargs(), return_lse=True)
+    # log-sum-exp over the splits = the row's log-sum-exp
+    mx = lse64.max(axis=0)
+    safe = np.where(np.isneginf(mx), 0.0, mx)
+    tot = safe + np.log(np.exp(lse64 - safe).sum(axis=0))
+    tot = np.where(np.isneginf(mx), -np.inf, tot)
+    both_empty = np.isneginf(tot) & np.isneginf(ref_lse)
+    assert np.array_equal(np.isneginf(tot), np.isneginf(ref_lse)), "empty rows differ"
+    err = np.abs(np.where(both_empty, 0.0, tot - ref_lse))
+    log(f"  {name}: lse max_abs={err.max():.3e} (tol {LSE_TOL[case.dtype]:g})")
+    assert err.max() <= LSE_TOL[case.dtype]
+    # a split with no visible key has lse = -inf and a zero output
+    assert np.all(o64[np.isneginf(lse64)] == 0.0)
+    compare(comb, ref, case.dtype, what=f"{name} combined")
+    assert torch.equal(comb, one), "two-stage result differs from rel_attn_fwd"
+
+
+def test_one_split_writes_out():
+    case = make_config("decode_b64", scale=1 / 16)
+    kw = device_case(case)
+    out, ws, n = rel_attn_fwd_splits(**kw, num_splits=1)
+    one = rel_attn_fwd(**kw, num_splits=1)
+    torch.cuda.synchronize()
+    assert n == 1 and ws is None
+    assert torch.equal(out, one)
+    compare(out, oracle.oracle_attention(**case.kwargs()), case.dtype, what="one split")
+
