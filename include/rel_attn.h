@@ -64,7 +64,7 @@ extern "C" {
  * num_heads, num_kv_heads: query / KV heads; num_heads % num_kv_heads == 0.
  * max_kv_len:    longest KV length in the batch (>= 0).
  *
- * Returns a split count in [1, 128], or REL_ATTN_EINVAL. Host only; touches
+ * Returns a split count in [1, 512], or REL_ATTN_EINVAL. Host only; touches
  * no device.
  */
 int rel_attn_num_splits(int is_local, int batch_size, int max_query_len, int num_heads,
@@ -108,7 +108,7 @@ size_t rel_attn_workspace_bytes(int num_splits, int num_tokens, int num_heads, i
  *   rel_extent   >= 0; 0 means no bias.
  *   softmax_scale multiplies q.k (the bias is added unscaled).
  *   causal       0 or 1; window_left / window_right: -1 = unbounded side.
- *   num_splits   1..128: each query tile's key range is cut into this many
+ *   num_splits   1..512: each query tile's key range is cut into this many
  *                pieces whose partial results are merged with log-sum-exp.
  *                The result does not depend on it beyond rounding.
  *   stream       hipStream_t to enqueue on (NULL = default stream).
@@ -171,7 +171,7 @@ int rel_attn_fwd_splits(const void* q, const void* key_cache, const void* value_
  *
  * workspace: device memory, >= rel_attn_workspace_bytes(num_splits, ...)
  *            bytes, 16-byte aligned, read only.
- * num_splits: 2..128 (with one split there is nothing to merge).
+ * num_splits: 2..512 (with one split there is nothing to merge).
  * head_dim:  64 or 128. stream: hipStream_t (NULL = default stream).
  * Returns REL_ATTN_OK, REL_ATTN_EINVAL (bad size, NULL out with
  * num_tokens > 0, misaligned workspace), REL_ATTN_EUNSUPPORTED (dtype,

@@ -23,7 +23,7 @@ constexpr int kMinKeysPerSplit = 256;
 // 16 workgroups per compute unit, at least 1024 keys per split.
 constexpr int kDecodeTargetWorkgroups = 4096;
 constexpr int kDecodeMinKeysPerSplit = 1024;
-constexpr int kMaxSplits = 128;
+constexpr int kMaxSplits = 512;
 
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
 

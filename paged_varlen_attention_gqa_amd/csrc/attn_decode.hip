@@ -2,12 +2,12 @@
 // one 16-column MFMA tile, bf16, head_dim 128, block_size a power of two that
 // is a multiple of 16.
 //
-// A workgroup owns one (request, KV head, split); its NW waves stream
-// interleaved 16-key tiles of the split's key range, each wave with its own
-// online-softmax state, and merge through LDS at the end. Each wave has a
-// private ring of RING tile slots in LDS that buffer loads fill directly
-// (global -> LDS, no registers), RING - 1 tiles ahead of the arithmetic.
-// Per tile a wave:
+// Each wave owns one (request, KV head, split) and streams the split's
+// 16-key tiles on its own; the NW waves of a workgroup take NW neighbouring
+// KV heads of the same (request, split), so together they read NW * 256
+// contiguous bytes of every cache slot row. Each wave has a private ring of
+// RING tile slots in LDS that buffer loads fill directly (global -> LDS, no
+// registers), RING - 1 tiles ahead of the arithmetic. Per tile a wave:
 //   * reads K from LDS as bf16 MFMA A operands (lane: key l%16, 8 dims at
 //     32c + 8(l/16)) and computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16
 //     (lane: column l%16, keys 4(l/16)+i); scale, relative bias, masks and
@@ -33,7 +33,8 @@ constexpr int kD = 128;
 constexpr int kTile = 16;
 constexpr int kRowBytes = kD * 2;              // one key row of K or V in LDS
 constexpr int kHalfSlot = kTile * kRowBytes;   // K (or V) part of a slot: 4 KB
-constexpr int kSlotBytes = 2 * kHalfSlot;      // one tile: K then V, 8 KB
+constexpr int kBiasOff = 2 * kHalfSlot;        // bias part of a slot: 16 B per lane
+constexpr int kSlotBytes = kBiasOff + 64 * 16;  // one tile: K, V, bias; 9 KB
 // A running max is kept until a tile's max exceeds it by this much (log2
 // units), so that the accumulator rescale is rare; probabilities stay below
 // 2^8.
@@ -45,9 +46,6 @@ constexpr float kRescaleSlack = 8.0f;
 #endif
 #ifndef REL_ATTN_DECODE_RING
 #define REL_ATTN_DECODE_RING 2
-#endif
-#ifndef REL_ATTN_DECODE_HEADS_FIRST
-#define REL_ATTN_DECODE_HEADS_FIRST 1
 #endif
 constexpr int kDecodeWaves = REL_ATTN_DECODE_WAVES;
 constexpr int kDecodeRing = REL_ATTN_DECODE_RING;
@@ -70,34 +68,18 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char* lds, ui
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds, 16, voff, 0, 0, 0);
 }
 
+// block_table is passed again as a restrict-qualified argument so that page
+// lookups compile to scalar loads: they then count on the scalar/LDS counter
+// and a wait for them never waits for the K/V copies in flight.
 template <int NW, int RING>
-__global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams P) {
+__global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams P,
+                                                              const int32_t* __restrict__ block_table) {
   // One LDS object per ring slot, so that the compiler waits for exactly the
   // copies a read depends on; wave w owns bytes [w*8K, (w+1)*8K) of each.
   __shared__ __attribute__((aligned(1024))) char ring0[NW * kSlotBytes];
   __shared__ __attribute__((aligned(1024))) char ring1[NW * kSlotBytes];
   __shared__ __attribute__((aligned(1024))) char ring2[RING > 2 ? NW * kSlotBytes : 16];
-  __shared__ float m_lds[NW][16];
-  __shared__ float l_lds[NW][16];
   static_assert(RING == 2 || RING == 3, "ring depth");
-
-#if REL_ATTN_DECODE_HEADS_FIRST
-  // the KV heads of one (request, split) are neighbours in launch order, so
-  // they walk the same pages at about the same time (DRAM row locality: the
-  // heads of one slot share a cache row)
-  const int b = blockIdx.z;
-  const int g = blockIdx.x;
-  const int split = blockIdx.y;
-#else
-  const int b = blockIdx.z;
-  const int g = blockIdx.y;
-  const int split = blockIdx.x;
-#endif
-  int t0, S, L;
-  if (!request_bounds(P, b, t0, S, L)) return;
-  const int G = P.G;
-  const int rows = S * G;
-  if (rows > 16) return;  // handled by the general kernel
 
   const int tid = threadIdx.x;
   // wave index as a scalar, so that the tile loop runs on the scalar unit
@@ -105,6 +87,16 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams P) {
   const int lane = tid & 63;
   const int n = lane & 15;  // column (query row) / K row / transpose-read lane
   const int q = lane >> 4;  // 0..3
+
+  const int b = blockIdx.z;
+  const int split = blockIdx.y;
+  const int g = blockIdx.x * NW + wave;  // KV head of this wave
+  if (g >= P.Hkv) return;
+  int t0, S, L;
+  if (!request_bounds(P, b, t0, S, L)) return;
+  const int G = P.G;
+  const int rows = S * G;
+  if (rows > 16) return;  // handled by the general kernel
 
   // column n: token n / G of the request, query head g*G + n % G
   const bool col_ok = n < rows;
@@ -116,7 +108,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams P) {
   int row_lo = 0, row_hi = 0;
   if (col_ok) visible_range(P, p, L, row_lo, row_hi);
 
-  // key range of the workgroup: union over its first and last token
+  // key range of the request's rows: union over its first and last token
   int lo_a, hi_a, lo_b, hi_b;
   visible_range(P, L - S, L, lo_a, hi_a);
   visible_range(P, L - 1, L, lo_b, hi_b);
@@ -124,14 +116,14 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams P) {
   const int wg_hi = max(hi_a, hi_b);
   const int kstart = wg_lo & ~(kTile - 1);
   const int c0 = __builtin_amdgcn_readfirstlane(kstart + split * P.dec_chunk);
-  const int c1 = min(c0 + P.dec_chunk, wg_hi);
+  const int c1 = __builtin_amdgcn_readfirstlane(min(c0 + P.dec_chunk, wg_hi));
   const int ntiles = __builtin_amdgcn_readfirstlane(c1 > c0 ? (c1 - c0 + kTile - 1) / kTile : 0);
 
   if (ntiles == 0) {
     // No visible key: the row's output is zero, and an empty split still
-    // tells the combine step that it holds nothing. Lane (n, q) of wave 0
-    // writes dims 32q .. 32q+31 of column n.
-    if (wave == 0 && col_ok) {
+    // tells the combine step that it holds nothing. Lane (n, q) writes dims
+    // 32q .. 32q+31 of column n.
+    if (col_ok) {
       if (P.splits == 1) {
         uint16_t* op = reinterpret_cast<uint16_t*>(P.out) + ((int64_t)t * P.H + h) * kD + 32 * q;
 #pragma unroll
@@ -181,10 +173,10 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams P) {
       v_rd[mb] = (uint32_t)(kHalfSlot + row * kRowBytes + 16 * ((2 * mb + ((n & 3) >> 1)) ^ swz(row)) + 8 * (n & 1));
   }
 
-  // relative-bias rows of this workgroup's columns: one resource from the
-  // first column's row, lane offsets relative to it
+  // relative-bias rows of this wave's columns: one resource from the first
+  // column's row, lane offsets relative to it
   const int E = P.E;
-  const int Em1 = E > 0 ? E - 1 : 0;
+  const int Em8 = E >= 8 ? E - 8 : 0;  // last start of 8 entries inside a row
   const char* rel_base = E > 0 ? reinterpret_cast<const char*>(P.rel) + ((int64_t)t0 * P.H + g * G) * E * 2
                                : reinterpret_cast<const char*>(P.q);
   const uint32_t rel_lane = E > 0 ? (uint32_t)((itok * P.H + hh) * E) * 2u : 0u;
@@ -192,17 +184,8 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams P) {
 
   const int bs_log2 = P.bs_log2;
   const int bs_mask = P.bs - 1;
-  const int32_t* bt_row = P.block_table + (int64_t)b * P.max_blocks;
-  const int npages_req = (L + P.bs - 1) >> bs_log2;
-
-  // page ids of the split, 64 at a time: lane i holds page pbase + i
-  int pbase = c0 >> bs_log2;
-  auto load_pages = [&](int first) -> int {
-    const int idx = first + lane;
-    int pg = idx < npages_req ? bt_row[idx] : 0;
-    return pg < 0 ? 0 : (pg >= P.num_blocks ? P.num_blocks - 1 : pg);
-  };
-  int pages = load_pages(pbase);
+  const int32_t* __restrict__ bt_row = block_table + (int64_t)b * P.max_blocks;
+  const int last_pidx = (c1 - 1) >> bs_log2;  // last page the split reads
 
   const char* kbytes = reinterpret_cast<const char*>(P.k);
   const char* vbytes = reinterpret_cast<const char*>(P.v);
@@ -211,36 +194,39 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams P) {
   char* const my1 = ring1 + wave * kSlotBytes;
   char* const my2 = ring2 + (RING > 2 ? wave * kSlotBytes : 0);
 
-  // keys that can carry a bias for some column: (p_min - E, p_max]
-  const int band_lo = __builtin_amdgcn_readfirstlane((L - S) - E + 1);
-  const int band_hi = __builtin_amdgcn_readfirstlane(L - 1);
+  // raw page-table entry of the tile at key j0 (a scalar load; pages past
+  // the split's last one are clamped to it); issue() clamps the id
+  auto page_at = [&](int j0) -> int {
+    int pidx = j0 >> bs_log2;
+    pidx = pidx > last_pidx ? last_pidx : pidx;
+    return bt_row[pidx];
+  };
 
-  // start the copy of the tile at key j0 into a slot; its bias goes to bias[]
-  auto issue = [&](char* slot, uint32_t (&bias)[4], int j0) {
-    // Bias first: the copies issued after it are then the only loads a later
-    // wait has to leave in flight, whether or not this tile loaded a bias.
-    // Four consecutive distances, clamped into the row (always in bounds);
-    // the arithmetic drops the ones outside [0, E).
-    if (E > 0 && j0 + kTile > band_lo && j0 <= band_hi) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = p - (j0 + 4 * q + i);
-        const int dc = d < 0 ? 0 : (d > Em1 ? Em1 : d);
-        bias[i] = __builtin_amdgcn_raw_buffer_load_b16(rel_rsrc, rel_lane + 2u * dc, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bias[i] = 0u;
-    }
-    const int pidx = j0 >> bs_log2;
-    if (pidx - pbase >= 64) {
-      pbase = pidx;
-      pages = load_pages(pbase);
-    }
-    const int page = __builtin_amdgcn_readlane(pages, pidx - pbase);
+  // The bias of lane (q, n) for the tile at j0: keys j0 + 4q + i (i = 0..3)
+  // have distances D - i, D = p - j0 - 4q, i.e. entries D-3 .. D of the
+  // column's rel_logits row. The copy moves 8 entries from a start clamped
+  // into the row (always in bounds) into the lane's 16 bytes of the slot;
+  // entries that the clamp shifted out are outside [0, E) and dropped by the
+  // arithmetic.
+  auto bias_start = [&](int j0) -> int {
+    const int d = p - (j0 + 4 * q) - 3;
+    return d < 0 ? 0 : (d > Em8 ? Em8 : d);
+  };
+
+  // Page ids are scalar loads issued one or two steps before the copy that
+  // uses them; after the loop the prefetched values are consumed, which keeps
+  // the compiler from sinking the loads next to their use.
+  auto keep = [](int v) { asm volatile("; page %0" ::"s"(v)); };
+
+  // start the copy of the tile at key j0 (raw page-table entry given) into a
+  // slot: 4 KB of K, 4 KB of V, 1 KB of bias. Every call issues the same
+  // nine copies, so the compiler's wait counts stay exact.
+  auto issue = [&](char* slot, int j0, int page) {
+    page = page < 0 ? 0 : (page >= P.num_blocks ? P.num_blocks - 1 : page);
     const int64_t base = (((int64_t)page << bs_log2) + (j0 & bs_mask)) * row_bytes + head_bytes;
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbytes + base);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbytes + base);
+    dma16(rel_rsrc, slot + kBiasOff, rel_lane + 2u * (uint32_t)bias_start(j0));
 #pragma unroll
     for (int r = 0; r < 4; ++r) dma16(kr, slot + 1024 * r, cp_off[r]);
 #pragma unroll
@@ -255,7 +241,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams P) {
   float m_ref = kNegInf;  // per column (lanes with equal n agree)
   float l_part = 0.f;     // this lane's share of the column's sum
 
-  auto compute = [&](const char* slot, const uint32_t (&bias)[4], int j0) {
+  auto compute = [&](const char* slot, int j0) {
     // S^T = K Q^T
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -264,14 +250,17 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams P) {
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf),
                                                   __builtin_bit_cast(bf16x8_t, qreg[c]), s, 0, 0, 0);
     }
-    // branch-free, so that every lane consumes its bias registers on every
-    // path (a skipped use would leave the loads pending for the wait counter)
+    // entry of key j0 + 4q + i among the lane's 8 copied ones is sh - i
+    const int sh = p - (j0 + 4 * q) - bias_start(j0);
+    const uint16_t* my_bias = reinterpret_cast<const uint16_t*>(slot + kBiasOff + 16 * lane);
     float mx = kNegInf;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = j0 + 4 * q + i;
       const uint32_t in_range = (uint32_t)(p - j) < (uint32_t)E ? 0xffffffffu : 0u;
-      const float bv = __uint_as_float((bias[i] << 16) & in_range);
+      const int k = sh - i < 0 ? 0 : (sh - i > 7 ? 7 : sh - i);
+      const uint32_t bits = (uint32_t)my_bias[k] << 16;
+      const float bv = __uint_as_float(bits & in_range);
       const float v = fmaf(s[i], P.scale_log2, bv * kLog2e);
       const bool vis = (j >= row_lo) & (j < row_hi);
       s[i] = vis ? v : kNegInf;
@@ -312,121 +301,151 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams P) {
     }
   };
 
-  // ---- key loop: wave w owns tiles w, w+NW, ...; RING-1 tiles in flight ----
-  // Inside the loop every step issues one tile's copies unconditionally, so
-  // the compiler's wait counts stay exact (a conditional load would make it
-  // wait for the prefetch too); the last RING-1 tiles are computed after it.
+  // ---- key loop over the split's tiles; RING-1 tiles in flight ----
+  // The loop runs whole iterations only (no exit inside its body): each step
+  // copies one tile RING-1 ahead and loads the page id of the tile two
+  // steps later still; the remaining tiles are computed after it.
   {
-    const int nw = wave < ntiles ? (ntiles - wave + NW - 1) / NW : 0;
-    auto j0_of = [&](int i) { return c0 + kTile * (wave + NW * i); };
-    uint32_t b0[4], b1[4], b2[4];
+    const int nw = ntiles;
+    // tiles past the last (prefetches only) map to the last one: always
+    // inside the split's pages
+    const int i_max = nw - 1;
+    auto j0_of = [&](int i) { return c0 + kTile * (i < i_max ? i : i_max); };
+    // Before computing a tile, a wave waits for its own copies of it: until
+    // only the copies issued after them (9 per tile) are outstanding. The
+    // waits are explicit because the compiler does not see which LDS bytes
+    // a buffer-to-LDS copy writes.
     if constexpr (RING == 3) {
-      if (nw > 0) issue(my0, b0, j0_of(0));
-      if (nw > 1) issue(my1, b1, j0_of(1));
+      // iteration k: tiles 3k .. 3k+2 computed, 3k+2 .. 3k+4 copied
+      if (nw > 0) issue(my0, j0_of(0), page_at(j0_of(0)));
+      if (nw > 1) issue(my1, j0_of(1), page_at(j0_of(1)));
+      int pa = page_at(j0_of(2)), pb = page_at(j0_of(3)), pc = page_at(j0_of(4));
+      const int iters = nw >= 3 ? (nw - 2) / 3 : 0;
       int i = 0;
-      for (; i + 2 < nw; i += 3) {
-        issue(my2, b2, j0_of(i + 2));
-        compute(my0, b0, j0_of(i));
-        if (i + 3 >= nw) { compute(my1, b1, j0_of(i + 1)); compute(my2, b2, j0_of(i + 2)); i = nw; break; }
-        issue(my0, b0, j0_of(i + 3));
-        compute(my1, b1, j0_of(i + 1));
-        if (i + 4 >= nw) { compute(my2, b2, j0_of(i + 2)); compute(my0, b0, j0_of(i + 3)); i = nw; break; }
-        issue(my1, b1, j0_of(i + 4));
-        compute(my2, b2, j0_of(i + 2));
+      for (int k = 0; k < iters; ++k, i += 3) {
+        issue(my2, j0_of(i + 2), pa);
+        wait_vm<18>();
+        compute(my0, j0_of(i));
+        // the next iteration's page ids, issued after the compute's LDS
+        // reads have been waited for (scalar loads and LDS reads share a
+        // counter): they complete before its next wait, which follows the
+        // wait for a tile
+        __builtin_amdgcn_sched_barrier(0);
+        const int na = page_at(j0_of(i + 5)), nb = page_at(j0_of(i + 6)), nc = page_at(j0_of(i + 7));
+        issue(my0, j0_of(i + 3), pb);
+        wait_vm<18>();
+        compute(my1, j0_of(i + 1));
+        issue(my1, j0_of(i + 4), pc);
+        wait_vm<18>();
+        compute(my2, j0_of(i + 2));
+        pa = na;
+        pb = nb;
+        pc = nc;
       }
-      // 0..2 tiles left, in slots i%3 and (i+1)%3 (i is a multiple of 3 here)
-      if (i < nw) compute(my0, b0, j0_of(i));
-      if (i + 1 < nw) compute(my1, b1, j0_of(i + 1));
-    } else {
-      if (nw > 0) issue(my0, b0, j0_of(0));
-      int i = 0;
-      for (; i + 1 < nw; i += 2) {
-        issue(my1, b1, j0_of(i + 1));
-        compute(my0, b0, j0_of(i));
-        if (i + 2 >= nw) { compute(my1, b1, j0_of(i + 1)); i = nw; break; }
-        issue(my0, b0, j0_of(i + 2));
-        compute(my1, b1, j0_of(i + 1));
-      }
-      if (i < nw) compute(my0, b0, j0_of(i));
-    }
-    (void)b2;
-  }
-
-  // ---- merge the waves' partial states through LDS (slot 0 of each wave) ----
-  const float l_col = wave_sum_xor_16_32(l_part);
-  if (q == 0) {
-    m_lds[wave][n] = m_ref;
-    l_lds[wave][n] = l_col;
-  }
-  float* const o_my = reinterpret_cast<float*>(my0);  // [16 columns][kD] fp32
-#pragma unroll
-  for (int mb = 0; mb < kD / 16; ++mb)
-    *reinterpret_cast<f32x4_t*>(&o_my[n * kD + 16 * mb + 4 * q]) = oacc[mb];
-  __syncthreads();
-
-  // thread -> (column c, 8 dims); 16 columns x 16 dim groups
-  for (int item = tid; item < 256; item += NW * 64) {
-    const int c = item >> 4;
-    const int dg = item & 15;
-    if (c >= rows) break;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, m_lds[w][c]);
-    float acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    float Lsum = 0.f;
-    if (M != kNegInf) {
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float mw = m_lds[w][c];
-        if (mw == kNegInf) continue;
-        const float sc = exp2f(mw - M);
-        Lsum += l_lds[w][c] * sc;
-        const float* ow = reinterpret_cast<const float*>(ring0 + w * kSlotBytes) + c * kD + 8 * dg;
-        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(ow);
-        const f32x4_t bq = *reinterpret_cast<const f32x4_t*>(ow + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[e] = fmaf(a[e], sc, acc[e]);
-          acc[4 + e] = fmaf(bq[e], sc, acc[4 + e]);
+      keep(pa);
+      keep(pb);
+      keep(pc);
+      // tiles i, i+1 are copied (if they exist); at most two more remain
+      if (i + 2 < nw) {
+        issue(my2, j0_of(i + 2), pa);
+        wait_vm<18>();
+        compute(my0, j0_of(i));
+        if (i + 3 < nw) {
+          issue(my0, j0_of(i + 3), pb);
+          wait_vm<18>();
+          compute(my1, j0_of(i + 1));
+          wait_vm<9>();
+          compute(my2, j0_of(i + 2));
+          wait_vm<0>();
+          compute(my0, j0_of(i + 3));
+        } else {
+          wait_vm<9>();
+          compute(my1, j0_of(i + 1));
+          wait_vm<0>();
+          compute(my2, j0_of(i + 2));
         }
+      } else if (i + 1 < nw) {
+        wait_vm<9>();
+        compute(my0, j0_of(i));
+        wait_vm<0>();
+        compute(my1, j0_of(i + 1));
+      } else if (i < nw) {
+        wait_vm<0>();
+        compute(my0, j0_of(i));
+      }
+    } else {
+      // iteration k: tiles 2k, 2k+1 computed, 2k+1, 2k+2 copied
+      if (nw > 0) issue(my0, j0_of(0), page_at(j0_of(0)));
+      int pa = page_at(j0_of(1)), pb = page_at(j0_of(2));
+      const int iters = nw >= 1 ? (nw - 1) / 2 : 0;
+      int i = 0;
+      for (int k = 0; k < iters; ++k, i += 2) {
+        issue(my1, j0_of(i + 1), pa);
+        wait_vm<9>();
+        compute(my0, j0_of(i));
+        // the next iteration's page ids, issued after the compute's LDS
+        // reads have been waited for (scalar loads and LDS reads share a
+        // counter): they complete before its next wait, which follows the
+        // wait for a tile
+        __builtin_amdgcn_sched_barrier(0);
+        const int na = page_at(j0_of(i + 3)), nb = page_at(j0_of(i + 4));
+        issue(my0, j0_of(i + 2), pb);
+        wait_vm<9>();
+        compute(my1, j0_of(i + 1));
+        pa = na;
+        pb = nb;
+      }
+      keep(pa);
+      keep(pb);
+      // tile i is copied (if it exists); at most one more remains
+      if (i + 1 < nw) {
+        issue(my1, j0_of(i + 1), pa);
+        wait_vm<9>();
+        compute(my0, j0_of(i));
+        wait_vm<0>();
+        compute(my1, j0_of(i + 1));
+      } else if (i < nw) {
+        wait_vm<0>();
+        compute(my0, j0_of(i));
       }
     }
-    const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
-    const int ct = t0 + c / G;
-    const int ch = g * G + c % G;
-    // acc[e] holds dim 8*dg + e
-    if (P.splits == 1) {
-      uint16_t* op = reinterpret_cast<uint16_t*>(P.out) + ((int64_t)ct * P.H + ch) * kD + 8 * dg;
-      u32x4_t w = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
-                   pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
-      *reinterpret_cast<u32x4_t*>(op) = w;
-    } else {
-      const int64_t slot = ((int64_t)split * P.T + ct) * P.H + ch;
-      float* wo = P.ws_o + slot * kD + 8 * dg;
-      *reinterpret_cast<f32x4_t*>(wo) = f32x4_t{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-      *reinterpret_cast<f32x4_t*>(wo + 4) = f32x4_t{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
-      if (dg == 0) P.ws_lse[slot] = Lsum > 0.f ? (M + __log2f(Lsum)) * kLn2 : kNegInf;
-    }
+  }
+
+  // ---- epilogue: normalise and write this wave's columns ----
+  // lane (q, n) holds dims 16mb + 4q + i of column n; m_ref is the column's
+  // reference max (log2 units), the same in the four lanes of a column
+  const float l_col = wave_sum_xor_16_32(l_part);
+  if (!col_ok) return;
+  const float inv = l_col > 0.f ? 1.f / l_col : 0.f;
+  if (P.splits == 1) {
+    uint16_t* op = reinterpret_cast<uint16_t*>(P.out) + ((int64_t)t * P.H + h) * kD + 4 * q;
+#pragma unroll
+    for (int mb = 0; mb < kD / 16; ++mb)
+      *reinterpret_cast<u32x2_t*>(op + 16 * mb) =
+          u32x2_t{pack_bf16x2(oacc[mb][0] * inv, oacc[mb][1] * inv), pack_bf16x2(oacc[mb][2] * inv, oacc[mb][3] * inv)};
+  } else {
+    const int64_t slot = ((int64_t)split * P.T + t) * P.H + h;
+    float* wo = P.ws_o + slot * kD + 4 * q;
+#pragma unroll
+    for (int mb = 0; mb < kD / 16; ++mb) *reinterpret_cast<f32x4_t*>(wo + 16 * mb) = oacc[mb] * inv;
+    if (q == 0) P.ws_lse[slot] = l_col > 0.f ? (m_ref + __log2f(l_col)) * kLn2 : kNegInf;
   }
 }
 
 }  // namespace
 
 bool decode_supported(const AttnParams& P, int dtype_bf16, int head_dim) {
-  return dtype_bf16 && head_dim == kD && P.bs_log2 >= 4;
+  // the 16-byte bias copies need rows of at least 8 entries
+  return dtype_bf16 && head_dim == kD && P.bs_log2 >= 4 && (P.E == 0 || P.E >= 8);
 }
 
 int launch_decode(const AttnParams& P, int head_dim, hipStream_t stream) {
   (void)head_dim;
-#if REL_ATTN_DECODE_HEADS_FIRST
-  dim3 grid(P.Hkv, P.splits, P.B);
-#else
-  dim3 grid(P.splits, P.Hkv, P.B);
-#endif
+  // workgroup: kDecodeWaves neighbouring KV heads of one (request, split)
+  dim3 grid((P.Hkv + kDecodeWaves - 1) / kDecodeWaves, P.splits, P.B);
   if (P.B == 0) return 0;
-  hipLaunchKernelGGL((attn_decode_kernel<kDecodeWaves, kDecodeRing>), grid, dim3(kDecodeWaves * 64), 0, stream, P);
+  hipLaunchKernelGGL((attn_decode_kernel<kDecodeWaves, kDecodeRing>), grid, dim3(kDecodeWaves * 64), 0, stream, P,
+                     P.block_table);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

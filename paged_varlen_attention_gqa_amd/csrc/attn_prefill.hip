@@ -62,14 +62,6 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char* lds, ui
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds, 16, voff, 0, 0, 0);
 }
 
-// s_waitcnt with only the vector-memory count constrained (gfx9 encoding:
-// vmcnt low bits [3:0] and high bits [15:14], expcnt [6:4], lgkmcnt [11:8])
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
 // workgroup execution barrier without a memory fence; the empty asm keeps the
 // compiler from moving memory operations across it
 __device__ __forceinline__ void lds_barrier() {

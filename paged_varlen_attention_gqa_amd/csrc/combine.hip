@@ -12,9 +12,13 @@ namespace relattn {
 namespace {
 
 // One wave per (token, head); lanes own head_dim / 64 consecutive dims.
+// Lane l reads the log-sum-exps of splits l, l+64, ... (up to kMaxPerLane
+// of them, so at most 64 * kMaxPerLane splits).
+constexpr int kMaxPerLane = 8;
+
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void combine_kernel(AttnParams P) {
-  __shared__ float w_lds[4][128];
+  __shared__ float w_lds[4][64 * kMaxPerLane];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;  // t * H + h
@@ -23,9 +27,14 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams P) {
   const int64_t stride = nrows;  // between splits, in rows
   const int K = P.splits;
 
-  float l0 = lane < K ? P.ws_lse[(int64_t)lane * stride + row] : kNegInf;
-  float l1 = lane + 64 < K ? P.ws_lse[(int64_t)(lane + 64) * stride + row] : kNegInf;
-  float mx = fmaxf(l0, l1);
+  float l[kMaxPerLane];
+  float mx = kNegInf;
+#pragma unroll
+  for (int e = 0; e < kMaxPerLane; ++e) {
+    const int k = lane + 64 * e;
+    l[e] = k < K ? P.ws_lse[(int64_t)k * stride + row] : kNegInf;
+    mx = fmaxf(mx, l[e]);
+  }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
   constexpr int kPer = D / 64;
@@ -33,13 +42,17 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams P) {
 #pragma unroll
   for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
   if (mx != kNegInf) {
-    float w0 = __expf(l0 - mx), w1 = __expf(l1 - mx);
-    float sum = w0 + w1;
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < kMaxPerLane; ++e) {
+      l[e] = __expf(l[e] - mx);
+      sum += l[e];
+    }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
     const float inv = 1.f / sum;
-    w_lds[wave][lane] = w0 * inv;
-    w_lds[wave][lane + 64] = w1 * inv;
+#pragma unroll
+    for (int e = 0; e < kMaxPerLane; ++e) w_lds[wave][lane + 64 * e] = l[e] * inv;
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     for (int k = 0; k < K; ++k) {
@@ -69,6 +82,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams P) {
 int launch_combine(const AttnParams& P, int dtype_bf16, int head_dim, hipStream_t stream) {
   const int64_t rows = (int64_t)P.T * P.H;
   if (rows == 0) return 0;
+  if (P.splits > 64 * kMaxPerLane) return -1;
   dim3 grid((unsigned)((rows + 3) / 4));
   dim3 block(256);
   if (dtype_bf16) {

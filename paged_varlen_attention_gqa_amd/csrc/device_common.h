@@ -39,6 +39,20 @@ struct AttnParams {
   int kv_cap;                // keys a block-table row can address: min(max_blocks * bs, 2^31 - 1)
 };
 
+// s_waitcnt with only the vector-memory count constrained: wait until at
+// most N vector memory operations of this wave are outstanding (they complete
+// in issue order). gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
+// [6:4], lgkmcnt [11:8]; the other two fields are left at their maximum. The
+// empty asm statements keep the compiler from moving memory accesses (LDS
+// reads of the data being waited for) across the wait.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(HERE, "librelattn.so")
 
 FP32 = 0
 BF16 = 1
-MAX_SPLITS = 128
+MAX_SPLITS = 512
 
 _lib = None
 

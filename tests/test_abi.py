@@ -53,7 +53,7 @@ def test_num_splits_range_and_errors(lib):
     for args in [(0, 64, 1, 32, 8, 8192), (0, 1, 1, 32, 4, 262144), (0, 4, 2048, 64, 8, 6144),
                  (1, 64, 512, 32, 4, 32768), (0, 2, 17, 4, 2, 70), (0, 1, 1, 8, 8, 1 << 20)]:
         r = lib.rel_attn_num_splits(*args)
-        assert 1 <= r <= 128, (args, r)
+        assert 1 <= r <= relattn.MAX_SPLITS, (args, r)
     assert lib.rel_attn_num_splits(1, 1, 1, 32, 4, 262144) == 1  # local: one split
     # long batch-1 decode splits many ways; short keys are never split below 256 per split
     assert lib.rel_attn_num_splits(0, 1, 1, 32, 4, 262144) >= 32
@@ -86,7 +86,7 @@ def _fwd(lib, entry="rel_attn_fwd", **over):
 @pytest.mark.parametrize("over,code", [
     (dict(H=30, Hkv=4), -1),     # heads not divisible
     (dict(splits=0), -1),
-    (dict(splits=129), -1),
+    (dict(splits=513), -1),
     (dict(T=-1), -1),
     (dict(bs=0), -1),
     (dict(wl=-2), -1),
@@ -125,7 +125,7 @@ def _combine(lib, ws=16, wsb=1 << 30, out=16, dtype=1, T=4, H=8, D=128, splits=4
 
 @pytest.mark.parametrize("over,code", [
     (dict(splits=1), -1),         # nothing to merge
-    (dict(splits=129), -1),
+    (dict(splits=513), -1),
     (dict(T=-1), -1),
     (dict(H=0), -1),
     (dict(out=0), -1),

@@ -103,6 +103,14 @@ EDGE = [
          head_dim=128, block_size=16, rel_extent=64, window_size=(100, -1)),
     dict(name="fp32_d128_window", query_lens=[3, 20], kv_lens=[77, 20], num_heads=6, num_kv_heads=3,
          head_dim=128, block_size=16, rel_extent=40, window_size=(10, 0), dtype=torch.float32),
+    dict(name="decode_extent_2", query_lens=[1, 1, 2], kv_lens=[40, 300, 17], num_heads=8,
+         num_kv_heads=2, head_dim=128, block_size=16, rel_extent=2),
+    dict(name="decode_extent_7", query_lens=[1, 3, 1], kv_lens=[40, 300, 17], num_heads=8,
+         num_kv_heads=2, head_dim=128, block_size=16, rel_extent=7),
+    dict(name="decode_extent_8", query_lens=[1, 3, 1], kv_lens=[40, 300, 9], num_heads=8,
+         num_kv_heads=2, head_dim=128, block_size=16, rel_extent=8),
+    dict(name="decode_extent_9_first_rows", query_lens=[1, 1], kv_lens=[5, 600], num_heads=4,
+         num_kv_heads=1, head_dim=128, block_size=32, rel_extent=9),
     dict(name="fp32_noncausal_g4", query_lens=[1, 7], kv_lens=[90, 7], num_heads=8, num_kv_heads=2,
          head_dim=64, block_size=8, rel_extent=5, causal=False, dtype=torch.float32),
 ]
@@ -115,7 +123,7 @@ def test_edge(spec):
     _check(make_case(**spec))
 
 
-@pytest.mark.parametrize("splits", [1, 2, 3, 8, 37, 128])
+@pytest.mark.parametrize("splits", [1, 2, 3, 8, 37, 128, 300, 512])
 def test_split_counts(splits):
     case = make_case(name="splits", query_lens=[1, 1, 4, 1], kv_lens=[3000, 17, 700, 5000],
                      num_heads=16, num_kv_heads=4, head_dim=128, block_size=16, rel_extent=600)
