@@ -49,14 +49,20 @@ extern "C" {
 #define REL_ATTN_ELAUNCH (-4)       /* the HIP runtime rejected a kernel launch */
 
 /*
- * rel_attn_num_splits - how many pieces to cut each query tile's key range
- * into (split-KV), for a call with the given shape.
+ * rel_attn_num_splits - how many pieces to cut each request's key range into
+ * (split-KV), for a call with the given shape.
  *
- * Same inputs as `inkling_fa4_num_splits` (docs.vllm.ai, same module): it
- * counts the work units (requests x KV heads x query tiles) and splits long
- * key ranges until the launch has enough workgroups to fill the GPU, keeping
- * at least 256 keys per split; local (sliding-window) calls are not split,
- * as on that page. The constants are chosen for 256 compute units.
+ * Same inputs as `inkling_fa4_num_splits` (docs.vllm.ai, same module); local
+ * (sliding-window) calls are not split, as on that page. The constants are
+ * chosen for 256 compute units:
+ *   - decode-shaped calls (max_query_len * num_heads / num_kv_heads <= 16):
+ *     the decode kernel shares the batch's keys evenly among one round of
+ *     workgroups (4 KV heads each) and cuts a request into at most this many
+ *     pieces; the count leaves room for requests of unequal length, and
+ *     pieces hold at least 256 keys (max_kv_len / 256 + 1 at most);
+ *   - other calls: work units (requests x KV heads x 64-row query tiles)
+ *     are split until the launch has about 1024 workgroups, keeping at
+ *     least 256 keys per split.
  *
  * is_local:      non-zero when either window side is >= 0.
  * batch_size:    number of requests (>= 1).
@@ -108,9 +114,10 @@ size_t rel_attn_workspace_bytes(int num_splits, int num_tokens, int num_heads, i
  *   rel_extent   >= 0; 0 means no bias.
  *   softmax_scale multiplies q.k (the bias is added unscaled).
  *   causal       0 or 1; window_left / window_right: -1 = unbounded side.
- *   num_splits   1..512: each query tile's key range is cut into this many
- *                pieces whose partial results are merged with log-sum-exp.
- *                The result does not depend on it beyond rounding.
+ *   num_splits   1..512: the key range of a query tile (of a request, in
+ *                decode-shaped calls) is cut into at most this many pieces
+ *                whose partial results are merged with log-sum-exp. The
+ *                result does not depend on it beyond rounding.
  *   stream       hipStream_t to enqueue on (NULL = default stream).
  *
  * Workspace query: with workspace == NULL and workspace_needed != NULL the
@@ -142,14 +149,15 @@ int rel_attn_fwd(const void* q, const void* key_cache, const void* value_cache,
  * arguments, same checks, same return codes.
  *
  * With num_splits == 1 it is rel_attn_fwd (the result goes to `out`). With
- * num_splits > 1 it leaves `out` untouched and writes, for every split k,
- * token t and head h, the normalised partial output over the keys of split k
- * and its log-sum-exp into the workspace, laid out as
+ * num_splits > 1 it leaves `out` untouched and writes, for every split slot
+ * k, token t and head h, the normalised partial output over the keys of
+ * piece k and its log-sum-exp into the workspace, laid out as
  *   float o[num_splits][num_tokens][num_heads][head_dim], followed by
  *   float lse[num_splits][num_tokens][num_heads]
  * where lse is the natural-log log-sum-exp of the scores (softmax_scale * q.k
- * + bias) of the split's visible keys, -inf for a split with none (its o is
- * then zero). Every entry is written. rel_attn_combine then produces `out`.
+ * + bias) of the piece's visible keys, -inf for a slot with none. Every lse
+ * entry is written; o entries of a slot whose lse is -inf are unspecified.
+ * rel_attn_combine then produces `out`.
  * This is the split-KV scheme behind the num_splits argument of the
  * docs.vllm.ai `inkling_fa4_rel_attention` / `inkling_fa4_num_splits` pages.
  */

@@ -19,10 +19,14 @@ constexpr int kGeneralRows = 64;
 constexpr int kTargetWorkgroups = 1024;
 // Fewest keys worth giving one split.
 constexpr int kMinKeysPerSplit = 256;
-// Decode-shaped calls (one 16-column tile of query rows per KV head): about
-// 16 workgroups per compute unit, at least 1024 keys per split.
-constexpr int kDecodeTargetWorkgroups = 4096;
-constexpr int kDecodeMinKeysPerSplit = 1024;
+// Decode-shaped calls (one 16-column tile of query rows per KV head): the
+// balanced decode kernel runs one round of 512 workgroups (2 per compute unit
+// on 256 CUs), each over 4 KV heads; splits are the most pieces one request
+// may be cut into, with room for requests of unequal length, and a piece
+// should hold at least 256 keys.
+constexpr int kDecodeWorkgroups = 512;
+constexpr int kDecodeHeadsPerWorkgroup = 4;
+constexpr int kDecodeMinKeysPerPiece = 256;
 constexpr int kMaxSplits = 512;
 
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
@@ -37,16 +41,26 @@ extern "C" int rel_attn_num_splits(int is_local, int batch_size, int max_query_l
   if (is_local) return 1;
   const int64_t G = num_heads / num_kv_heads;
   const int64_t rows = (int64_t)max_query_len * G;
-  const bool decode = rows <= relattn::kDecodeMaxRows;
-  const int64_t qtiles = decode ? 1 : (rows + kGeneralRows - 1) / kGeneralRows;
+  if (rows <= relattn::kDecodeMaxRows) {
+    // the workgroups of one KV head group share the batch's tiles evenly; a
+    // request of the longest length then spans about (workgroups per group)
+    // / batch pieces if all requests were that long; four times that leaves
+    // room for shorter neighbours
+    const int64_t groups = (num_kv_heads + kDecodeHeadsPerWorkgroup - 1) / kDecodeHeadsPerWorkgroup;
+    const int64_t per_group = kDecodeWorkgroups / groups > 0 ? kDecodeWorkgroups / groups : 1;
+    int64_t splits = (4 * per_group + batch_size - 1) / batch_size + 2;
+    const int64_t by_len = max_kv_len / kDecodeMinKeysPerPiece + 1;
+    if (splits > by_len) splits = by_len;
+    if (splits > kMaxSplits) splits = kMaxSplits;
+    if (splits < 1) splits = 1;
+    return (int)splits;
+  }
+  // Prefill-shaped calls: split long key ranges until the launch has about
+  // 4 workgroups per compute unit.
+  const int64_t qtiles = (rows + kGeneralRows - 1) / kGeneralRows;
   const int64_t units = (int64_t)batch_size * num_kv_heads * qtiles;
-  // Decode-shaped calls stream K/V at memory speed: many short splits keep
-  // every compute unit fed despite unequal request lengths. Prefill-shaped
-  // calls have work enough in their query tiles.
-  const int64_t target = decode ? kDecodeTargetWorkgroups : kTargetWorkgroups;
-  const int64_t min_keys = decode ? kDecodeMinKeysPerSplit : kMinKeysPerSplit;
-  int64_t splits = (target + units - 1) / units;
-  const int64_t by_len = max_kv_len / min_keys;
+  int64_t splits = (kTargetWorkgroups + units - 1) / units;
+  const int64_t by_len = max_kv_len / kMinKeysPerSplit;
   if (splits > by_len) splits = by_len;
   if (splits > kMaxSplits) splits = kMaxSplits;
   if (splits < 1) splits = 1;

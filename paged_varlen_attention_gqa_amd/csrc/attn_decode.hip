@@ -22,6 +22,8 @@
 // Score and bias rule: prhub.com.cn report on vLLM PR #48858, "key source
 // snippets" (score_mod_rel_bias); paged-cache layout and the split count:
 // docs.vllm.ai inkling_fa4_rel_attention / inkling_fa4_num_splits.
+#include <atomic>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -68,35 +70,23 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char* lds, ui
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds, 16, voff, 0, 0, 0);
 }
 
-// block_table is passed again as a restrict-qualified argument so that page
-// lookups compile to scalar loads: they then count on the scalar/LDS counter
-// and a wait for them never waits for the K/V copies in flight.
+// One wave's work on one piece of one request: the request's rows (S * G
+// <= 16 columns) against KV head g over the keys [c0, c1) (c0 a multiple of
+// 16 inside the request's visible range, c1 its end or a later multiple of
+// 16), written to `out` when the call has one split, else to split slot
+// `split` of the workspace (normalised partial output and log-sum-exp).
+// block_table is the same table as P.block_table, restrict-qualified so that
+// page lookups compile to scalar loads: they then count on the scalar/LDS
+// counter and a wait for them never waits for the K/V copies in flight.
 template <int NW, int RING>
-__global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams P,
-                                                              const int32_t* __restrict__ block_table) {
-  // One LDS object per ring slot, so that the compiler waits for exactly the
-  // copies a read depends on; wave w owns bytes [w*8K, (w+1)*8K) of each.
-  __shared__ __attribute__((aligned(1024))) char ring0[NW * kSlotBytes];
-  __shared__ __attribute__((aligned(1024))) char ring1[NW * kSlotBytes];
-  __shared__ __attribute__((aligned(1024))) char ring2[RING > 2 ? NW * kSlotBytes : 16];
-  static_assert(RING == 2 || RING == 3, "ring depth");
-
-  const int tid = threadIdx.x;
-  // wave index as a scalar, so that the tile loop runs on the scalar unit
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
+__device__ __forceinline__ void decode_piece(const AttnParams& P, const int32_t* __restrict__ block_table,
+                                             char* ring0, char* ring1, char* ring2, int wave, int lane,
+                                             int b, int g, int t0, int S, int L, int c0_in, int c1_in,
+                                             int split) {
   const int n = lane & 15;  // column (query row) / K row / transpose-read lane
   const int q = lane >> 4;  // 0..3
-
-  const int b = blockIdx.z;
-  const int split = blockIdx.y;
-  const int g = blockIdx.x * NW + wave;  // KV head of this wave
-  if (g >= P.Hkv) return;
-  int t0, S, L;
-  if (!request_bounds(P, b, t0, S, L)) return;
   const int G = P.G;
   const int rows = S * G;
-  if (rows > 16) return;  // handled by the general kernel
 
   // column n: token n / G of the request, query head g*G + n % G
   const bool col_ok = n < rows;
@@ -108,15 +98,8 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams P,
   int row_lo = 0, row_hi = 0;
   if (col_ok) visible_range(P, p, L, row_lo, row_hi);
 
-  // key range of the request's rows: union over its first and last token
-  int lo_a, hi_a, lo_b, hi_b;
-  visible_range(P, L - S, L, lo_a, hi_a);
-  visible_range(P, L - 1, L, lo_b, hi_b);
-  const int wg_lo = min(lo_a, lo_b);
-  const int wg_hi = max(hi_a, hi_b);
-  const int kstart = wg_lo & ~(kTile - 1);
-  const int c0 = __builtin_amdgcn_readfirstlane(kstart + split * P.dec_chunk);
-  const int c1 = __builtin_amdgcn_readfirstlane(min(c0 + P.dec_chunk, wg_hi));
+  const int c0 = __builtin_amdgcn_readfirstlane(c0_in);
+  const int c1 = __builtin_amdgcn_readfirstlane(c1_in);
   const int ntiles = __builtin_amdgcn_readfirstlane(c1 > c0 ? (c1 - c0 + kTile - 1) / kTile : 0);
 
   if (ntiles == 0) {
@@ -432,6 +415,153 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams P,
   }
 }
 
+// the key range of a request's rows: the union over its first and last
+// token, from a multiple of 16 (kstart) to hi; ntiles 16-key tiles
+__device__ __forceinline__ void request_keys(const AttnParams& P, int S, int L, int& kstart, int& hi, int& ntiles) {
+  int lo_a, hi_a, lo_b, hi_b;
+  visible_range(P, L - S, L, lo_a, hi_a);
+  visible_range(P, L - 1, L, lo_b, hi_b);
+  const int lo = min(lo_a, lo_b);
+  hi = max(hi_a, hi_b);
+  kstart = lo & ~(kTile - 1);
+  ntiles = hi > lo ? (hi - kstart + kTile - 1) / kTile : 0;
+}
+
+// One workgroup per (KV head group of NW heads, split, request): split s of
+// request b covers the keys [kstart + s * dec_chunk, + dec_chunk).
+template <int NW, int RING>
+__global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams P,
+                                                              const int32_t* __restrict__ block_table) {
+  // One LDS object per ring slot, so that the compiler keeps them apart;
+  // wave w owns bytes [w * kSlotBytes, (w + 1) * kSlotBytes) of each.
+  __shared__ __attribute__((aligned(1024))) char ring0[NW * kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char ring1[NW * kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char ring2[RING > 2 ? NW * kSlotBytes : 16];
+  static_assert(RING == 2 || RING == 3, "ring depth");
+  // wave index as a scalar, so that the tile loop runs on the scalar unit
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.z;
+  const int split = blockIdx.y;
+  const int g = blockIdx.x * NW + wave;  // KV head of this wave
+  if (g >= P.Hkv) return;
+  int t0, S, L;
+  if (!request_bounds(P, b, t0, S, L)) return;
+  if (S * P.G > 16) return;  // handled by the prefill or general kernel
+  int kstart, hi, ntiles;
+  request_keys(P, S, L, kstart, hi, ntiles);
+  const int c0 = kstart + split * P.dec_chunk;
+  decode_piece<NW, RING>(P, block_table, ring0, ring1, ring2, wave, lane, b, g, t0, S, L, c0,
+                         min(c0 + P.dec_chunk, hi), split);
+}
+
+// Balanced split of the whole batch (at most 64 requests, num_splits >= 2):
+// the decode-shaped requests' 16-key tiles are laid end to end (N of them)
+// and workgroup m of a KV head group takes tiles [m N / M, (m+1) N / M), M
+// the number of workgroups used, so every workgroup streams the same number
+// of tiles whatever the lengths. A request's tiles then fall to consecutive
+// workgroups; the piece of the k-th of them goes to split slot k. M is the
+// largest launched count for which no request has more than num_splits
+// pieces. Slots a request does not use get lse = -inf.
+template <int NW, int RING>
+__global__ __launch_bounds__(NW * 64) void attn_decode_balanced_kernel(AttnParams P,
+                                                                       const int32_t* __restrict__ block_table) {
+  __shared__ __attribute__((aligned(1024))) char ring0[NW * kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char ring1[NW * kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char ring2[RING > 2 ? NW * kSlotBytes : 16];
+  static_assert(RING == 2 || RING == 3, "ring depth");
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x;
+  const int M = gridDim.x;
+  const int g = blockIdx.y * NW + wave;  // KV head of this wave
+  if (g >= P.Hkv) return;
+  const int K = P.splits;
+
+  // lane l describes request l: first row, rows, keys, key range and tiles
+  int t0_l = 0, S_l = 0, L_l = 0, ks_l = 0, hi_l = 0, n_l = 0;
+  bool dec_l = false;  // a decode-shaped request with rows
+  if (lane < P.B) {
+    int t0, S, L;
+    if (request_bounds(P, lane, t0, S, L) && S * P.G <= 16) {
+      dec_l = true;
+      t0_l = t0;
+      S_l = S;
+      L_l = L;
+      request_keys(P, S, L, ks_l, hi_l, n_l);
+    }
+  }
+  // prefix sums of the tile counts over the requests
+  int incl = n_l;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  const int excl = incl - n_l;
+  const int N = __builtin_amdgcn_readlane(incl, 63);
+  int nmax = n_l;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) nmax = max(nmax, __shfl_xor(nmax, off));
+  nmax = __builtin_amdgcn_readfirstlane(nmax);
+
+  // workgroups used: pieces per request <= ceil((n - 1) / (N / Me)) + 1 <= K
+  // when every workgroup gets at least ceil(nmax / (K - 1)) tiles
+  int Me = 1;
+  if (N > 0) {
+    const int qmin = (nmax + K - 2) / (K - 1);
+    Me = N / qmin;
+    Me = Me < 1 ? 1 : (Me > M ? M : Me);
+  }
+  if (m >= Me) return;
+  const int a_lo = (int)((int64_t)m * N / Me);
+  const int a_hi = (int)((int64_t)(m + 1) * N / Me);
+
+  const int n = lane & 15;
+  // all K slots (or those after slot k0) of request b get lse = -inf
+  auto clear_slots = [&](int bt0, int brows, int k0) {
+    if (n < brows) {
+      const int t = bt0 + n / P.G;
+      const int h = g * P.G + n % P.G;
+      for (int k = k0 + (lane >> 4); k < K; k += 4) P.ws_lse[((int64_t)k * P.T + t) * P.H + h] = kNegInf;
+    }
+  };
+
+  // requests without visible keys: the workgroup whose range holds their
+  // position in the tile sequence (the last one for position N) clears them
+  {
+    const bool mine = dec_l && n_l == 0 && ((excl >= a_lo && excl < a_hi) || (m == Me - 1 && excl >= a_hi));
+    uint64_t mask = __builtin_amdgcn_ballot_w64(mine);
+    while (mask) {
+      const int bb = __builtin_ctzll(mask);
+      mask &= mask - 1;
+      clear_slots(__builtin_amdgcn_readlane(t0_l, bb), __builtin_amdgcn_readlane(S_l, bb) * P.G, 0);
+    }
+  }
+
+  // the requests whose tiles meet [a_lo, a_hi), in order
+  uint64_t mask = __builtin_amdgcn_ballot_w64(n_l > 0 && incl > a_lo && excl < a_hi);
+  while (mask) {
+    const int bb = __builtin_ctzll(mask);
+    mask &= mask - 1;
+    const int bt0 = __builtin_amdgcn_readlane(t0_l, bb);
+    const int bS = __builtin_amdgcn_readlane(S_l, bb);
+    const int bL = __builtin_amdgcn_readlane(L_l, bb);
+    const int bks = __builtin_amdgcn_readlane(ks_l, bb);
+    const int bhi = __builtin_amdgcn_readlane(hi_l, bb);
+    const int bn = __builtin_amdgcn_readlane(n_l, bb);
+    const int bex = __builtin_amdgcn_readlane(excl, bb);
+    const int u0 = max(a_lo, bex) - bex;
+    const int u1 = min(a_hi, bex + bn) - bex;
+    // piece index: workgroups from the one holding the request's first tile
+    const int m_first = (int)(((int64_t)(bex + 1) * Me - 1) / N);
+    const int k = m - m_first;
+    decode_piece<NW, RING>(P, block_table, ring0, ring1, ring2, wave, lane, bb, g, bt0, bS, bL,
+                           bks + kTile * u0, min(bks + kTile * u1, bhi), k);
+    if (u1 == bn) clear_slots(bt0, bS * P.G, k + 1);
+  }
+}
+
 }  // namespace
 
 bool decode_supported(const AttnParams& P, int dtype_bf16, int head_dim) {
@@ -439,13 +569,45 @@ bool decode_supported(const AttnParams& P, int dtype_bf16, int head_dim) {
   return dtype_bf16 && head_dim == kD && P.bs_log2 >= 4 && (P.E == 0 || P.E >= 8);
 }
 
+namespace {
+
+// workgroups of the balanced kernel resident at once on the device (all its
+// compute units), queried once per device
+int balanced_slots() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(attn_decode_balanced_kernel<kDecodeWaves, kDecodeRing>),
+          kDecodeWaves * 64, 0) != hipSuccess)
+    return 0;
+  v = cus * per_cu;
+  cached[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+}  // namespace
+
 int launch_decode(const AttnParams& P, int head_dim, hipStream_t stream) {
   (void)head_dim;
-  // workgroup: kDecodeWaves neighbouring KV heads of one (request, split)
-  dim3 grid((P.Hkv + kDecodeWaves - 1) / kDecodeWaves, P.splits, P.B);
   if (P.B == 0) return 0;
-  hipLaunchKernelGGL((attn_decode_kernel<kDecodeWaves, kDecodeRing>), grid, dim3(kDecodeWaves * 64), 0, stream, P,
-                     P.block_table);
+  const int groups = (P.Hkv + kDecodeWaves - 1) / kDecodeWaves;
+  if (P.splits > 1 && P.B <= 64) {
+    const int slots = balanced_slots();
+    if (slots <= 0) return -1;
+    // one round of workgroups over the whole device
+    const int per_group = slots / groups > 0 ? slots / groups : 1;
+    hipLaunchKernelGGL((attn_decode_balanced_kernel<kDecodeWaves, kDecodeRing>), dim3(per_group, groups),
+                       dim3(kDecodeWaves * 64), 0, stream, P, P.block_table);
+  } else {
+    // workgroup: kDecodeWaves neighbouring KV heads of one (request, split)
+    hipLaunchKernelGGL((attn_decode_kernel<kDecodeWaves, kDecodeRing>), dim3(groups, P.splits, P.B),
+                       dim3(kDecodeWaves * 64), 0, stream, P, P.block_table);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

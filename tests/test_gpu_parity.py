@@ -111,6 +111,9 @@ EDGE = [
          num_kv_heads=2, head_dim=128, block_size=16, rel_extent=8),
     dict(name="decode_extent_9_first_rows", query_lens=[1, 1], kv_lens=[5, 600], num_heads=4,
          num_kv_heads=1, head_dim=128, block_size=32, rel_extent=9),
+    dict(name="decode_b80_mixed_lengths", query_lens=[1] * 76 + [2, 3, 1, 4],
+         kv_lens=[(37 * i) % 700 + 1 for i in range(80)], num_heads=16, num_kv_heads=4, head_dim=128,
+         block_size=16, rel_extent=64),
     dict(name="fp32_noncausal_g4", query_lens=[1, 7], kv_lens=[90, 7], num_heads=8, num_kv_heads=2,
          head_dim=64, block_size=8, rel_extent=5, causal=False, dtype=torch.float32),
 ]
@@ -125,6 +128,8 @@ def test_edge(spec):
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 8, 37, 128, 300, 512])
 def test_split_counts(splits):
+    """Any split count gives the same result (the balanced decode kernel for
+    this batch: at most 64 requests)."""
     case = make_case(name="splits", query_lens=[1, 1, 4, 1], kv_lens=[3000, 17, 700, 5000],
                      num_heads=16, num_kv_heads=4, head_dim=128, block_size=16, rel_extent=600)
     _check(case, num_splits=splits, what=f"splits={splits}")

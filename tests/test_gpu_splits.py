@@ -5,7 +5,7 @@ Checked against the fp64 oracle: the log-sum-exp over the splits of each row
 must equal the row's full log-sum-exp, and the combined output must equal
 both the oracle's output (at the parity tolerance) and rel_attn_fwd's output
 bit for bit (the one-call entry point launches the same kernels). The
-workspace is filled with NaN first, so an entry left unwritten shows up.
+workspace is filled with NaN first, so a log-sum-exp left unwritten shows up.
 """
 
 import numpy as np
@@ -39,9 +39,11 @@ def _two_stage(case, splits):
     o, lse = split_partials(ws, splits, T, H, D)
     o64 = o.cpu().double().numpy()
     lse64 = lse.cpu().double().numpy()
-    assert not np.isnan(o64).any() and not np.isnan(lse64).any(), "unwritten workspace entries"
-    assert np.all(np.isfinite(o64))
+    # every lse entry is written; o is defined where lse is finite
+    assert not np.isnan(lse64).any(), "unwritten log-sum-exp entries"
     assert not np.isposinf(lse64).any()
+    used = np.isfinite(lse64)
+    assert np.all(np.isfinite(o64[used]))
     comb = rel_attn_combine(ws, torch.empty_like(kw["q"]), splits)
     one = rel_attn_fwd(**kw, num_splits=splits)
     torch.cuda.synchronize()
@@ -77,8 +79,6 @@ def test_split_stage_then_combine(name, mk, splits):
     err = np.abs(np.where(both_empty, 0.0, tot - ref_lse))
     log(f"  {name}: lse max_abs={err.max():.3e} (tol {LSE_TOL[case.dtype]:g})")
     assert err.max() <= LSE_TOL[case.dtype]
-    # a split with no visible key has lse = -inf and a zero output
-    assert np.all(o64[np.isneginf(lse64)] == 0.0)
     compare(comb, ref, case.dtype, what=f"{name} combined")
     assert torch.equal(comb, one), "two-stage result differs from rel_attn_fwd"
 
