@@ -75,8 +75,8 @@ STAGE_SOURCES = {
     "tiny_fp32": ["attn_general.hip"],
 }
 STAGE_KERNELS = {
-    "decode_b64": "attn_decode_kernel",
-    "decode_long_b1": "attn_decode_kernel",
+    "decode_b64": "attn_decode_balanced_kernel",
+    "decode_long_b1": "attn_decode_balanced_kernel",
     "prefill_chunked": "attn_decode_kernel (no work: rows > 16) + attn_prefill_kernel",
     "mixed_window": "attn_decode_kernel + attn_prefill_kernel",
     "tiny_fp32": "attn_general_kernel",
