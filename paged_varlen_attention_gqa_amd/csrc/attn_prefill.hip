@@ -47,19 +47,35 @@ constexpr float kRescaleSlack = 8.0f;     // log2 units, as in the decode kernel
 typedef __bf16 bf16x8v_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+// Buffer resource (base, size in bytes; out-of-range reads return 0) as the
+// four scalar words of the descriptor.
+__device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
 }
+
 
 // chunk swizzle of K/V LDS row r: a bijection of 0..15 that keeps 16
 // consecutive rows on distinct chunks and maps rows 4a..4a+3 to chunks that
 // differ in bits 1..3
 __device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char* lds, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds, 16, voff, 0, 0, 0);
+// global -> LDS copy of 1 KB per instruction: lane l writes bytes
+// [16l, 16l+16) of the LDS block at lds. Issued from inline assembly so that
+// the compiler does not guard the LDS reads with waits of its own: it cannot
+// tell which LDS bytes such a copy writes, and its conservative waits (for
+// copies into other buffers) would stall the prefetch. Every read of copied
+// data is preceded by an explicit wait_vm<N> and a barrier instead. The
+// statement sets M0 (the copy's LDS base) itself; nothing else in this
+// kernel keeps a value in M0.
+__device__ __forceinline__ void dma16(const u32x4_t rsrc, char* lds, uint32_t voff) {
+  const uint32_t m0v = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0v), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+#pragma clang diagnostic pop
 }
 
 // workgroup execution barrier without a memory fence; the empty asm keeps the
@@ -86,13 +102,10 @@ __device__ __forceinline__ float lane_swap32_sum(float v) {
 // it also wait for the copies in flight)
 __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
                                                                  const int32_t* __restrict__ block_table) {
-  // one LDS object per buffer, so that the compiler waits for exactly the
-  // copies a read depends on
-  __shared__ __attribute__((aligned(1024))) char kv0[kKV];
-  __shared__ __attribute__((aligned(1024))) char kv1[kKV];
-  __shared__ __attribute__((aligned(1024))) char bias0[kWaves * kBiasWave];
-  __shared__ __attribute__((aligned(1024))) char bias1[kWaves * kBiasWave];
-  __shared__ __attribute__((aligned(1024))) char bias2[kWaves * kBiasWave];
+  // two K/V tile buffers, then three bias buffers
+  __shared__ __attribute__((aligned(1024))) char lds[2 * kKV + 3 * kWaves * kBiasWave];
+  char* const kv_buf = lds;
+  char* const bias_buf = lds + 2 * kKV;
 
   const int b = blockIdx.z;
   const int g = blockIdx.y;
@@ -149,6 +162,11 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
       if (row_ok) v = *reinterpret_cast<const u32x4_t*>(qp + 16 * kk + 8 * h);
       qreg[kk] = v;
     }
+    // wait for q here, once: the compiler does not count the copies issued
+    // in the key loop, so a first use of q inside the loop would come with a
+    // wait for every copy in flight
+#pragma unroll
+    for (int kk = 0; kk < kD / 16; ++kk) asm volatile("" ::"v"(qreg[kk]));
   }
 
   // ---- K/V copy geometry ----
@@ -224,7 +242,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
     if (E == 0) reg_lo = reg_hi = 0;
   }
   const char* rel_base = E > 0 ? reinterpret_cast<const char*>(P.rel) + reg_lo * 2 : reinterpret_cast<const char*>(P.q);
-  const __amdgpu_buffer_rsrc_t rel_rsrc = make_rsrc(rel_base, (uint32_t)((reg_hi - reg_lo) * 2));
+  const u32x4_t rel_rsrc = make_rsrc(rel_base, (uint32_t)((reg_hi - reg_lo) * 2));
   const int64_t my_row_abs = (int64_t)t * P.H + hq;
   const int rel_lane_elem = (int)(my_row_abs * E - reg_lo);  // row start, relative to the resource
   // Pieces can straddle the resource only at the two ends of the whole
@@ -267,8 +285,8 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
     page = page < 0 ? 0 : (page >= P.num_blocks ? P.num_blocks - 1 : page);
     page = __builtin_amdgcn_readfirstlane(page);
     const int64_t base = (((int64_t)page << bs_log2) + (key0 & bs_mask)) * row_bytes + head_bytes;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbytes + base, 0x7fffffffu);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbytes + base, 0x7fffffffu);
+    const u32x4_t kr = make_rsrc(kbytes + base, 0x7fffffffu);
+    const u32x4_t vr = make_rsrc(vbytes + base, 0x7fffffffu);
 #pragma unroll
     for (int c4 = 0; c4 < 2; ++c4) dma16(kr, kv + k_dst[c4], k_src[c4]);
 #pragma unroll
@@ -297,6 +315,14 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   float l_part = 0.f;     // this lane's share of the column sum
   const float scale_log2 = P.scale_log2;  // scores are acc * scale_log2 (bias included)
 
+  // One tile. Masks are applied in branches that keep their computation
+  // inside (the empty asm statements stop the compiler from turning them
+  // into selects computed on every tile): score masks only on tiles some row
+  // does not see whole, bias masks only where the band covers part of the
+  // tile, the edge-row patch only in waves holding the first or last row of
+  // rel_logits. Scores stay unscaled (the scale is positive) until the
+  // exponent, so that the scale costs no extra instruction per score.
+  const bool edge_wave = __builtin_amdgcn_ballot_w64(edge_row) != 0;
   auto compute = [&](const char* kv, const char* bias, int j0) {
     // S^T = K Q^T (+ bias / scale) for the two 32-key halves
     const int bc = band_class(j0);
@@ -316,58 +342,68 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
         s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, kf),
                                                         __builtin_bit_cast(bf16x8v_t, qreg[kk]), s[st], 0, 0, 0);
       }
+    if (bc != 0) {
+      // piece q = 2st + u: entry x is distance e_lo(q) + x (key 32st + 16u + 8h + 7 - x)
+      u32x4_t bb[4];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      if (bc != 0) {
+      for (int q = 0; q < 4; ++q) bb[q] = *reinterpret_cast<const u32x4_t*>(my_bias + 1024 * q + 16 * lane);
+      const int e_lo0 = p - (j0 + 8 * h) - 7;
+      if (bc == 2) {
+        asm volatile("");
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          // entry x of this lane's piece is distance e_lo + x (key 32st + 16u + 8h + 7 - x)
-          u32x4_t bb = *reinterpret_cast<const u32x4_t*>(my_bias + 1024 * (2 * st + u) + 16 * lane);
-          const int e_lo = p - (j0 + 32 * st + 16 * u + 8 * h) - 7;
-          if (bc == 2) {
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              const uint32_t lo_ok = (uint32_t)(e_lo + 2 * w) < (uint32_t)E ? 0xffffu : 0u;
-              const uint32_t hi_ok = (uint32_t)(e_lo + 2 * w + 1) < (uint32_t)E ? 0xffff0000u : 0u;
-              bb[w] &= lo_ok | hi_ok;
-            }
+          for (int w = 0; w < 4; ++w) {
+            const int e = e_lo0 - 16 * q + 2 * w;
+            const uint32_t lo_ok = (uint32_t)e < (uint32_t)E ? 0xffffu : 0u;
+            const uint32_t hi_ok = (uint32_t)(e + 1) < (uint32_t)E ? 0xffff0000u : 0u;
+            bb[q][w] &= lo_ok | hi_ok;
           }
-          if (__builtin_amdgcn_ballot_w64(edge_row) != 0) {
-            // rows at the very start or end of the tensor: re-read their
-            // in-range entries one by one (clamped reads, kept where in range)
-            const uint16_t* rrow = reinterpret_cast<const uint16_t*>(P.rel) + (edge_row ? my_row_abs * E : 0);
+      }
+      if (edge_wave) {
+        asm volatile("");
+        // rows at the very start or end of the tensor: re-read their
+        // in-range entries one by one (clamped reads, kept where in range)
+        const uint16_t* rrow = reinterpret_cast<const uint16_t*>(P.rel) + (edge_row ? my_row_abs * E : 0);
 #pragma unroll
-            for (int x = 0; x < 8; ++x) {
-              const int d = e_lo + x;
-              const bool keep = edge_row && d >= 0 && d < E;
-              const uint32_t v = rrow[keep ? d : 0];
-              const uint32_t w = bb[x >> 1];
-              const uint32_t nw = (x & 1) ? ((w & 0xffffu) | (v << 16)) : ((w & 0xffff0000u) | v);
-              bb[x >> 1] = keep ? nw : w;
-            }
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            const int d = e_lo0 - 16 * q + x;
+            const bool keep = edge_row && d >= 0 && d < E;
+            const uint32_t v = rrow[keep ? d : 0];
+            const uint32_t w = bb[q][x >> 1];
+            const uint32_t nw = (x & 1) ? ((w & 0xffffu) | (v << 16)) : ((w & 0xffff0000u) | v);
+            bb[q][x >> 1] = keep ? nw : w;
           }
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
           s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, bias_sel[u]),
-                                                          __builtin_bit_cast(bf16x8v_t, bb), s[st], 0, 0, 0);
-        }
+                                                          __builtin_bit_cast(bf16x8v_t, bb[2 * st + u]), s[st], 0, 0, 0);
+    }
+    // masks (register a of half st is key j0 + 32st + 16h + a), then the row
+    // max of the unscaled scores, scaled (log2 units)
+    const bool interior = (j0 >= lo_max) && (j0 + kKeys <= hi_min);
+    if (!interior) {
+      asm volatile("");
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        // visible registers: row_lo - jb <= a < row_hi - jb
+        const int jb = j0 + 32 * st + 16 * h;
+        const int a_lo = row_lo - jb, a_hi = row_hi - jb;
+#pragma unroll
+        for (int a = 0; a < 16; ++a) s[st][a] = (a >= a_lo && a < a_hi) ? s[st][a] : kNegInf;
       }
     }
-    // scale and mask (log2 units); register a of half st is key j0 + 32st + 16h + a
-    const bool interior = (j0 >= lo_max) && (j0 + kKeys <= hi_min);
     float mx = kNegInf;
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int jb = j0 + 32 * st + 16 * h;
-      // visible registers: row_lo - jb <= a < row_hi - jb
-      const int a_lo = row_lo - jb, a_hi = row_hi - jb;
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        float v = s[st][a] * scale_log2;
-        if (!interior) v = (a >= a_lo && a < a_hi) ? v : kNegInf;
-        s[st][a] = v;
-        mx = fmaxf(mx, v);
-      }
-    }
-    if (interior && !row_ok) mx = kNegInf;
+      for (int a = 0; a < 16; ++a) mx = fmaxf(mx, s[st][a]);
+    mx = row_ok ? mx * scale_log2 : kNegInf;
     mx = lane_swap32_max(mx);
     if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleSlack) != 0) {
       const float m_new = fmaxf(m_ref, mx);
@@ -378,15 +414,12 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
       for (int mt = 0; mt < kD / 32; ++mt) oacc[mt] *= alpha;
     }
     const float m_use = m_ref == kNegInf ? 0.f : m_ref;
-    // keys past L may hold anything (NaN) and 0 * NaN = NaN: zero their V
-    // elements in the operand
-    const bool tail = j0 + kKeys > L;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       // probabilities as the B operand of PV: block kb takes registers 8kb..8kb+7
 #pragma unroll
       for (int a = 0; a < 16; ++a) {
-        const float e = __builtin_amdgcn_exp2f(s[st][a] - m_use);
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[st][a], scale_log2, -m_use));
         s[st][a] = e;
         l_part += e;
       }
@@ -403,12 +436,6 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
             const char* addr = kv + kHalf + (32 * st + 8 * kb + 4 * sr) * kRowBytes + v_rd[c];
             part[sr] = __builtin_bit_cast(
                 u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)addr));
-            if (tail) {
-              // this lane received keys 32st + 16h + 8kb + 4sr + (0..3)
-              const int k0 = j0 + 32 * st + 16 * h + 8 * kb + 4 * sr;
-              part[sr][0] &= (k0 < L ? 0xffffu : 0u) | (k0 + 1 < L ? 0xffff0000u : 0u);
-              part[sr][1] &= (k0 + 2 < L ? 0xffffu : 0u) | (k0 + 3 < L ? 0xffff0000u : 0u);
-            }
           }
           const u32x4_t av = {part[0][0], part[0][1], part[1][0], part[1][1]};
           oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, av),
@@ -416,6 +443,24 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
         }
       }
     }
+  };
+
+  // The tile holding key L - 1 may hold keys past L, whose V rows may be
+  // anything (NaN) while their probabilities are 0 (0 * NaN = NaN): once it
+  // is in LDS the workgroup overwrites those rows with zeros. Thread i
+  // clears 16 bytes of rows i/16 and i/16 + 32.
+  auto zero_v_tail = [&](char* kv, int j0) {
+    const int r_from = L - j0;  // rows r_from .. 63 hold keys past L
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int r = (tid >> 4) + 32 * pass;
+      if (r >= r_from) *reinterpret_cast<u32x4_t*>(kv + kHalf + r * kRowBytes + 16 * (tid & 15)) = u32x4_t{0u, 0u, 0u, 0u};
+    }
+    // the stores have landed before the barrier (lgkmcnt(0) only)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
+    lds_barrier();
   };
 
   // ---- key loop ----
@@ -426,9 +471,9 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   if (tile_begin < tile_end) {
     const int last = tile_end - 1;
     auto j0_of = [&](int it) { return kstart + kKeys * min(it, last); };
-    issue_kv(kv0, j0_of(tile_begin));
-    issue_bias(bias0, j0_of(tile_begin));
-    issue_bias(bias1, j0_of(tile_begin + 1));
+    issue_kv(kv_buf, j0_of(tile_begin));
+    issue_bias(bias_buf, j0_of(tile_begin));
+    issue_bias(bias_buf + kWaves * kBiasWave, j0_of(tile_begin + 1));
     // One stage: copy ahead, then use tile it (K/V buffer it%2, bias it%3).
     // The workgroup barriers carry no memory fence (a fence would wait for
     // the copies just issued): each wave first waits for its own copies of
@@ -436,27 +481,23 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
     // K/V it+1, bias it+2: 4 each) are outstanding, and LDS reads finish
     // before a wave reaches the second barrier because their results are
     // consumed by then.
-    auto stage = [&](char* kv_cur, char* b_cur, char* kv_next, char* b_next2, int it) {
+    int kv_i = 0, b_i = 0;  // buffers of tile it
+    for (int it = tile_begin; it < tile_end; ++it) {
+      char* const kv_cur = kv_buf + kv_i * kKV;
+      char* const kv_next = kv_buf + (kv_i ^ 1) * kKV;
+      const int b_n2 = b_i == 0 ? 2 : b_i - 1;  // (b_i + 2) % 3
+      char* const b_cur = bias_buf + b_i * (kWaves * kBiasWave);
+      char* const b_next2 = bias_buf + b_n2 * (kWaves * kBiasWave);
       issue_kv(kv_next, j0_of(it + 1));
       issue_bias(b_next2, j0_of(it + 2));
       wait_vm<12>();
       lds_barrier();  // tile it is in LDS for every wave
-      compute(kv_cur, b_cur, j0_of(it));
-      lds_barrier();  // everyone is done with the buffers tile it+2 / it+3 will reuse
-    };
-    for (int it = tile_begin;; it += 6) {
-      stage(kv0, bias0, kv1, bias2, it);
-      if (it + 1 >= tile_end) break;
-      stage(kv1, bias1, kv0, bias0, it + 1);
-      if (it + 2 >= tile_end) break;
-      stage(kv0, bias2, kv1, bias1, it + 2);
-      if (it + 3 >= tile_end) break;
-      stage(kv1, bias0, kv0, bias2, it + 3);
-      if (it + 4 >= tile_end) break;
-      stage(kv0, bias1, kv1, bias0, it + 4);
-      if (it + 5 >= tile_end) break;
-      stage(kv1, bias2, kv0, bias1, it + 5);
-      if (it + 6 >= tile_end) break;
+      const int j0 = j0_of(it);
+      if (j0 + kKeys > L) zero_v_tail(kv_cur, j0);
+      compute(kv_cur, b_cur, j0);
+      lds_barrier();  // everyone is done with the buffers tiles it+2 / it+3 will reuse
+      kv_i ^= 1;
+      b_i = b_i == 2 ? 0 : b_i + 1;
     }
     // the last copies re-read tiles nobody uses: let them land before the
     // LDS is released
@@ -499,7 +540,8 @@ bool prefill_supported(const AttnParams& P, int dtype_bf16, int head_dim) {
   // resource offsets are 32-bit: the bias rows of one wave must span less
   // than 2 GB (E * H * (32/G + 2) entries)
   const int64_t span = (int64_t)P.E * P.H * (32 / P.G + 2) * 2 + 256;
-  return dtype_bf16 && head_dim == kD && P.bs_log2 >= 4 && span < 0x7fffffff;
+  // the scores stay unscaled until the exponent: the scale must be positive
+  return dtype_bf16 && head_dim == kD && P.bs_log2 >= 4 && span < 0x7fffffff && P.scale_log2 > 0.f;
 }
 
 int launch_prefill(const AttnParams& P, hipStream_t stream) {
