@@ -37,11 +37,13 @@ namespace {
 constexpr int kD = 128;
 constexpr int kWaves = 8;
 constexpr int kRowsWG = 32 * kWaves;  // packed query rows per workgroup
-constexpr int kKeys = 64;             // keys per tile
+constexpr int kKeys = 32;             // keys per tile
 constexpr int kRowBytes = kD * 2;
-constexpr int kHalf = kKeys * kRowBytes;  // K (or V) part of a tile: 16 KB
-constexpr int kKV = 2 * kHalf;            // 32 KB
-constexpr int kBiasWave = 32 * kKeys * 2;  // one wave's bias slice of a tile: 4 KB
+constexpr int kHalf = kKeys * kRowBytes;  // K (or V) part of a tile: 8 KB
+constexpr int kKV = 2 * kHalf;            // 16 KB
+constexpr int kBiasWave = 32 * kKeys * 2;  // one wave's bias slice of a tile: 2 KB
+constexpr int kKvSlots = 4;               // K/V ring: copies 3 tiles ahead
+constexpr int kBiasSlots = 6;             // bias ring: copies 5 tiles ahead
 constexpr float kRescaleSlack = 8.0f;     // log2 units, as in the decode kernel
 
 typedef __bf16 bf16x8v_t __attribute__((ext_vector_type(8)));
@@ -102,10 +104,10 @@ __device__ __forceinline__ float lane_swap32_sum(float v) {
 // it also wait for the copies in flight)
 __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
                                                                  const int32_t* __restrict__ block_table) {
-  // two K/V tile buffers, then three bias buffers
-  __shared__ __attribute__((aligned(1024))) char lds[2 * kKV + 3 * kWaves * kBiasWave];
+  // the K/V ring, then the bias ring (160 KB)
+  __shared__ __attribute__((aligned(1024))) char lds[kKvSlots * kKV + kBiasSlots * kWaves * kBiasWave];
   char* const kv_buf = lds;
-  char* const bias_buf = lds + 2 * kKV;
+  char* const bias_buf = lds + kKvSlots * kKV;
 
   const int b = blockIdx.z;
   const int g = blockIdx.y;
@@ -170,33 +172,31 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   }
 
   // ---- K/V copy geometry ----
-  // wave w copies keys 8w..8w+7 of the tile (inside one page segment) with
-  // two instructions for K and two for V; instruction c4 covers keys
-  // 8w + 4c4 + (0..3), lane l one 16-byte chunk of key 8w + 4c4 + l/16.
-  // K key 32st + 16h' + 4i + kk goes to LDS row 32st + 8i + 4h' + kk.
+  // wave w copies keys 4w..4w+3 of the tile (inside one page segment) with
+  // one instruction for K and one for V; lane l copies one 16-byte chunk of
+  // key 4w + l/16. K key 16h' + 4i + kk goes to LDS row 8i + 4h' + kk, so
+  // that output register a of lane (h, n) of the QK MFMA is key 16h + a.
   const uint32_t row_bytes = (uint32_t)P.Hkv * kD * 2;
-  uint32_t k_src[2], v_src[2];
-  int k_dst[2], v_dst[2];
-#pragma unroll
-  for (int c4 = 0; c4 < 2; ++c4) {
-    const int key = 8 * wave + 4 * c4;  // first key of the instruction (tile-relative)
-    const int st = key >> 5, kap = key & 31;
-    const int krow0 = 32 * st + 8 * ((kap & 15) >> 2) + 4 * (kap >> 4);
+  uint32_t k_src, v_src;
+  int k_dst, v_dst;
+  {
+    const int key = 4 * wave;  // first key of the wave's copy (tile-relative)
+    const int krow0 = 8 * ((key & 15) >> 2) + 4 * (key >> 4);
     const int krow = krow0 + (lane >> 4);
     const int vrow = key + (lane >> 4);
-    k_src[c4] = (uint32_t)(4 * c4 + (lane >> 4)) * row_bytes + 16u * (uint32_t)((lane & 15) ^ swz(krow));
-    v_src[c4] = (uint32_t)(4 * c4 + (lane >> 4)) * row_bytes + 16u * (uint32_t)((lane & 15) ^ swz(vrow));
-    k_dst[c4] = krow0 * kRowBytes;
-    v_dst[c4] = kHalf + key * kRowBytes;
+    k_src = (uint32_t)(lane >> 4) * row_bytes + 16u * (uint32_t)((lane & 15) ^ swz(krow));
+    v_src = (uint32_t)(lane >> 4) * row_bytes + 16u * (uint32_t)((lane & 15) ^ swz(vrow));
+    k_dst = krow0 * kRowBytes;
+    v_dst = kHalf + key * kRowBytes;
   }
-  // K operand read of step kk: row 32st + n, logical chunk 2kk + h; the
+  // K operand read of step kk: row n, logical chunk 2kk + h; the
   // chunk is (2kk) ^ (h ^ swz(n)) as 2kk and h occupy disjoint bits
   uint32_t k_rd[kD / 16];
 #pragma unroll
   for (int kk = 0; kk < kD / 16; ++kk)
     k_rd[kk] = (uint32_t)(n * kRowBytes + 16 * ((2 * kk) ^ (h ^ swz(n & 15))));
-  // transpose reads of V for (half st, block kb, dim tile mt, group sr): lane
-  // (h, n), j = n%16, points at row 32st + 16h + 8kb + 4sr + j/4 and element
+  // transpose reads of V for (block kb, dim tile mt, group sr): lane
+  // (h, n), j = n%16, points at row 16h + 8kb + 4sr + j/4 and element
   // 32mt + 16(n/16) + 4(j%4). The row's swizzle is 8sr + 2(j/4) + kb, so the
   // chunk is Y ^ (4mt ^ 8sr ^ kb) with Y = 2(n/16) + (j%4)/2 ^ 2(j/4): one
   // lane value XOR a constant of (mt, sr, kb).
@@ -216,16 +216,23 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   const int bs_mask = P.bs - 1;
   const int32_t* __restrict__ bt_row = block_table + (int64_t)b * P.max_blocks;
   const int last_page = ((L > 0 ? L : 1) - 1) >> bs_log2;
+  // raw page-table entry of this wave's keys of the tile at j0 (a scalar
+  // load; keys past L map to the request's last page)
+  auto page_of = [&](int j0) -> int {
+    int pidx = (j0 + 4 * wave) >> bs_log2;
+    pidx = pidx > last_page ? last_page : pidx;
+    return bt_row[pidx];
+  };
   const char* kbytes = reinterpret_cast<const char*>(P.k);
   const char* vbytes = reinterpret_cast<const char*>(P.v);
   const int64_t head_bytes = (int64_t)g * kD * 2;
 
   // ---- relative-bias copy geometry ----
-  // The wave's slice of a tile: for each (half st, part u, lane half h) the
-  // 8 entries d = p - (j0 + 32st + 16u + 8h) - 7 .. +7 of each of its 32 rows,
-  // i.e. the bias of keys 32st + 16u + 8h + 7 - x for entry x. LDS layout
-  // [st][u][h][row n] x 16 bytes, so instruction q = 2st + u writes 1 KB in
-  // lane order (lane = 32h + n): each lane copies for its own column n.
+  // The wave's slice of a tile: for each (part u, lane half h) the 8 entries
+  // d = p - (j0 + 16u + 8h) - 7 .. +7 of each of its 32 rows, i.e. the bias
+  // of keys 16u + 8h + 7 - x for entry x. LDS layout [u][h][row n] x 16
+  // bytes, so instruction u writes 1 KB in lane order (lane = 32h + n): each
+  // lane copies for its own column n.
   // Copies read through one resource over the wave's rows plus 64 entries
   // on each side (inside the tensor); pieces outside it read as zeros.
   const int E = P.E;
@@ -249,7 +256,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   // tensor: lanes of the first or last tensor row fix their values in
   // registers.
   const bool edge_row = E > 0 && row_ok && (my_row_abs == 0 || my_row_abs == (int64_t)P.T * P.H - 1);
-  // distances covered by a tile over the workgroup's rows: [p_lo - j0 - 63, p_hi - j0]
+  // distances covered by a tile over the workgroup's rows: [p_lo - j0 - 31, p_hi - j0]
   const int p_lo = ia + L - S, p_hi = ib + L - S;
   // 0: no key of the tile gets a bias, 1: every score does, 2: some do
   auto band_class = [&](int j0) -> int {
@@ -277,21 +284,13 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
     }
   }
 
-  auto issue_kv = [&](char* kv, int j0) {
-    const int key0 = j0 + 8 * wave;
-    int pidx = key0 >> bs_log2;
-    pidx = pidx > last_page ? last_page : pidx;  // keys past L: any valid page of the request
-    int page = bt_row[pidx];
+  auto issue_kv = [&](char* kv, int j0, int page) {
     page = page < 0 ? 0 : (page >= P.num_blocks ? P.num_blocks - 1 : page);
     page = __builtin_amdgcn_readfirstlane(page);
+    const int key0 = j0 + 4 * wave;
     const int64_t base = (((int64_t)page << bs_log2) + (key0 & bs_mask)) * row_bytes + head_bytes;
-    const u32x4_t kr = make_rsrc(kbytes + base, 0x7fffffffu);
-    const u32x4_t vr = make_rsrc(vbytes + base, 0x7fffffffu);
-#pragma unroll
-    for (int c4 = 0; c4 < 2; ++c4) dma16(kr, kv + k_dst[c4], k_src[c4]);
-#pragma unroll
-    for (int c4 = 0; c4 < 2; ++c4) dma16(vr, kv + v_dst[c4], v_src[c4]);
-    asm volatile("" ::: "memory");
+    dma16(make_rsrc(kbytes + base, 0x7fffffffu), kv + k_dst, k_src);
+    dma16(make_rsrc(vbytes + base, 0x7fffffffu), kv + v_dst, v_src);
   };
   auto issue_bias = [&](char* bias, int j0) {
     char* my_bias = bias + wave * kBiasWave;
@@ -299,11 +298,10 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
     // so that it costs no HBM traffic
     const bool no_bias = band_class(j0) == 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e_lo = no_bias ? 0 : p - (j0 + 16 * q + 8 * h) - 7;
-      dma16(rel_rsrc, my_bias + 1024 * q, (uint32_t)(rel_lane_elem + e_lo) * 2u);
+    for (int u = 0; u < 2; ++u) {
+      const int e_lo = no_bias ? 0 : p - (j0 + 16 * u + 8 * h) - 7;
+      dma16(rel_rsrc, my_bias + 1024 * u, (uint32_t)(rel_lane_elem + e_lo) * 2u);
     }
-    asm volatile("" ::: "memory");
   };
 
   f32x16_t oacc[kD / 32];  // O^T: dim tile mt, lane (h, n) reg a = dim 32mt + 8(a/4) + 4h + a%4
@@ -324,40 +322,34 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   // exponent, so that the scale costs no extra instruction per score.
   const bool edge_wave = __builtin_amdgcn_ballot_w64(edge_row) != 0;
   auto compute = [&](const char* kv, const char* bias, int j0) {
-    // S^T = K Q^T (+ bias / scale) for the two 32-key halves
+    // S^T = K Q^T (+ bias / scale); register a of lane (h, n) is key j0 + 16h + a
     const int bc = band_class(j0);
     const char* my_bias = bias + wave * kBiasWave;
-    f32x16_t s[2];
+    f32x16_t s;
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+    for (int a = 0; a < 16; ++a) s[a] = 0.f;
 #pragma unroll
-      for (int a = 0; a < 16; ++a) s[st][a] = 0.f;
-    // the two halves' MFMA chains are interleaved so that each MFMA issues
-    // while the previous one of the other chain is still in flight
-#pragma unroll
-    for (int kk = 0; kk < kD / 16; ++kk)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kv + 32 * st * kRowBytes + k_rd[kk]);
-        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, kf),
-                                                        __builtin_bit_cast(bf16x8v_t, qreg[kk]), s[st], 0, 0, 0);
-      }
+    for (int kk = 0; kk < kD / 16; ++kk) {
+      const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kv + k_rd[kk]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, kf),
+                                                  __builtin_bit_cast(bf16x8v_t, qreg[kk]), s, 0, 0, 0);
+    }
     if (bc != 0) {
-      // piece q = 2st + u: entry x is distance e_lo(q) + x (key 32st + 16u + 8h + 7 - x)
-      u32x4_t bb[4];
+      // piece u: entry x is distance e_lo0 - 16u + x (key 16u + 8h + 7 - x)
+      u32x4_t bb[2];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) bb[q] = *reinterpret_cast<const u32x4_t*>(my_bias + 1024 * q + 16 * lane);
+      for (int u = 0; u < 2; ++u) bb[u] = *reinterpret_cast<const u32x4_t*>(my_bias + 1024 * u + 16 * lane);
       const int e_lo0 = p - (j0 + 8 * h) - 7;
       if (bc == 2) {
         asm volatile("");
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            const int e = e_lo0 - 16 * q + 2 * w;
+            const int e = e_lo0 - 16 * u + 2 * w;
             const uint32_t lo_ok = (uint32_t)e < (uint32_t)E ? 0xffffu : 0u;
             const uint32_t hi_ok = (uint32_t)(e + 1) < (uint32_t)E ? 0xffff0000u : 0u;
-            bb[q][w] &= lo_ok | hi_ok;
+            bb[u][w] &= lo_ok | hi_ok;
           }
       }
       if (edge_wave) {
@@ -366,43 +358,35 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
         // in-range entries one by one (clamped reads, kept where in range)
         const uint16_t* rrow = reinterpret_cast<const uint16_t*>(P.rel) + (edge_row ? my_row_abs * E : 0);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int x = 0; x < 8; ++x) {
-            const int d = e_lo0 - 16 * q + x;
+            const int d = e_lo0 - 16 * u + x;
             const bool keep = edge_row && d >= 0 && d < E;
             const uint32_t v = rrow[keep ? d : 0];
-            const uint32_t w = bb[q][x >> 1];
+            const uint32_t w = bb[u][x >> 1];
             const uint32_t nw = (x & 1) ? ((w & 0xffffu) | (v << 16)) : ((w & 0xffff0000u) | v);
-            bb[q][x >> 1] = keep ? nw : w;
+            bb[u][x >> 1] = keep ? nw : w;
           }
       }
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, bias_sel[u]),
-                                                          __builtin_bit_cast(bf16x8v_t, bb[2 * st + u]), s[st], 0, 0, 0);
+      for (int u = 0; u < 2; ++u)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, bias_sel[u]),
+                                                    __builtin_bit_cast(bf16x8v_t, bb[u]), s, 0, 0, 0);
     }
-    // masks (register a of half st is key j0 + 32st + 16h + a), then the row
-    // max of the unscaled scores, scaled (log2 units)
+    // masks, then the row max of the unscaled scores, scaled (log2 units)
     const bool interior = (j0 >= lo_max) && (j0 + kKeys <= hi_min);
     if (!interior) {
       asm volatile("");
+      // visible registers: row_lo - jb <= a < row_hi - jb
+      const int jb = j0 + 16 * h;
+      const int a_lo = row_lo - jb, a_hi = row_hi - jb;
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        // visible registers: row_lo - jb <= a < row_hi - jb
-        const int jb = j0 + 32 * st + 16 * h;
-        const int a_lo = row_lo - jb, a_hi = row_hi - jb;
-#pragma unroll
-        for (int a = 0; a < 16; ++a) s[st][a] = (a >= a_lo && a < a_hi) ? s[st][a] : kNegInf;
-      }
+      for (int a = 0; a < 16; ++a) s[a] = (a >= a_lo && a < a_hi) ? s[a] : kNegInf;
     }
     float mx = kNegInf;
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int a = 0; a < 16; ++a) mx = fmaxf(mx, s[st][a]);
+    for (int a = 0; a < 16; ++a) mx = fmaxf(mx, s[a]);
     mx = row_ok ? mx * scale_log2 : kNegInf;
     mx = lane_swap32_max(mx);
     if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleSlack) != 0) {
@@ -414,33 +398,30 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
       for (int mt = 0; mt < kD / 32; ++mt) oacc[mt] *= alpha;
     }
     const float m_use = m_ref == kNegInf ? 0.f : m_ref;
+    // probabilities as the B operand of PV: block kb takes registers 8kb..8kb+7
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      // probabilities as the B operand of PV: block kb takes registers 8kb..8kb+7
+    for (int a = 0; a < 16; ++a) {
+      const float e = __builtin_amdgcn_exp2f(fmaf(s[a], scale_log2, -m_use));
+      s[a] = e;
+      l_part += e;
+    }
 #pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[st][a], scale_log2, -m_use));
-        s[st][a] = e;
-        l_part += e;
-      }
+    for (int kb = 0; kb < 2; ++kb) {
+      const u32x4_t pb = {pack_bf16x2(s[8 * kb + 0], s[8 * kb + 1]), pack_bf16x2(s[8 * kb + 2], s[8 * kb + 3]),
+                          pack_bf16x2(s[8 * kb + 4], s[8 * kb + 5]), pack_bf16x2(s[8 * kb + 6], s[8 * kb + 7])};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const u32x4_t pb = {pack_bf16x2(s[st][8 * kb + 0], s[st][8 * kb + 1]), pack_bf16x2(s[st][8 * kb + 2], s[st][8 * kb + 3]),
-                            pack_bf16x2(s[st][8 * kb + 4], s[st][8 * kb + 5]), pack_bf16x2(s[st][8 * kb + 6], s[st][8 * kb + 7])};
+      for (int mt = 0; mt < kD / 32; ++mt) {
+        u32x2_t part[2];
 #pragma unroll
-        for (int mt = 0; mt < kD / 32; ++mt) {
-          u32x2_t part[2];
-#pragma unroll
-          for (int sr = 0; sr < 2; ++sr) {
-            const int c = kb | ((mt & 1) << 1) | ((((mt >> 1) ^ sr) & 1) << 2);
-            const char* addr = kv + kHalf + (32 * st + 8 * kb + 4 * sr) * kRowBytes + v_rd[c];
-            part[sr] = __builtin_bit_cast(
-                u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)addr));
-          }
-          const u32x4_t av = {part[0][0], part[0][1], part[1][0], part[1][1]};
-          oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, av),
-                                                             __builtin_bit_cast(bf16x8v_t, pb), oacc[mt], 0, 0, 0);
+        for (int sr = 0; sr < 2; ++sr) {
+          const int c = kb | ((mt & 1) << 1) | ((((mt >> 1) ^ sr) & 1) << 2);
+          const char* addr = kv + kHalf + (8 * kb + 4 * sr) * kRowBytes + v_rd[c];
+          part[sr] = __builtin_bit_cast(
+              u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)addr));
         }
+        const u32x4_t av = {part[0][0], part[0][1], part[1][0], part[1][1]};
+        oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, av),
+                                                           __builtin_bit_cast(bf16x8v_t, pb), oacc[mt], 0, 0, 0);
       }
     }
   };
@@ -448,15 +429,11 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   // The tile holding key L - 1 may hold keys past L, whose V rows may be
   // anything (NaN) while their probabilities are 0 (0 * NaN = NaN): once it
   // is in LDS the workgroup overwrites those rows with zeros. Thread i
-  // clears 16 bytes of rows i/16 and i/16 + 32.
+  // clears 16 bytes of row i/16.
   auto zero_v_tail = [&](char* kv, int j0) {
-    const int r_from = L - j0;  // rows r_from .. 63 hold keys past L
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      const int r = (tid >> 4) + 32 * pass;
-      if (r >= r_from) *reinterpret_cast<u32x4_t*>(kv + kHalf + r * kRowBytes + 16 * (tid & 15)) = u32x4_t{0u, 0u, 0u, 0u};
-    }
+    const int r_from = L - j0;  // rows r_from .. 31 hold keys past L
+    const int r = threadIdx.x >> 4;
+    if (r >= r_from) *reinterpret_cast<u32x4_t*>(kv + kHalf + r * kRowBytes + 16 * (threadIdx.x & 15)) = u32x4_t{0u, 0u, 0u, 0u};
     // the stores have landed before the barrier (lgkmcnt(0) only)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
@@ -464,40 +441,45 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   };
 
   // ---- key loop ----
-  // K/V tiles are double buffered (copied one tile ahead), bias slices triple
-  // buffered (two tiles ahead: the bias stream has no reuse and comes from
-  // HBM). Copies past the last tile re-read it, so that every stage issues
-  // the same loads and the compiler's wait counts stay exact.
+  // Rings in LDS: K/V tiles are copied 3 tiles ahead (4 slots), bias slices
+  // 5 tiles ahead (6 slots; the bias stream has no reuse and comes from
+  // HBM); page ids are loaded a stage before the copy that uses them. A
+  // stage waits for the wave's own copies of tile it, i.e. until only the 10
+  // copies issued after them are outstanding (bias it+2, then K/V and bias of
+  // tiles it+1 / it+3 and it+2 / it+4: 2 each), then meets the other waves at
+  // a barrier without a memory fence (a fence would wait for every copy in
+  // flight). Past the barrier every wave is done with tile it-1, whose slots
+  // then take tiles it+3 and it+5. Copies past the last tile re-read it, so
+  // that every stage issues the same copies.
   if (tile_begin < tile_end) {
     const int last = tile_end - 1;
     auto j0_of = [&](int it) { return kstart + kKeys * min(it, last); };
-    issue_kv(kv_buf, j0_of(tile_begin));
-    issue_bias(bias_buf, j0_of(tile_begin));
-    issue_bias(bias_buf + kWaves * kBiasWave, j0_of(tile_begin + 1));
-    // One stage: copy ahead, then use tile it (K/V buffer it%2, bias it%3).
-    // The workgroup barriers carry no memory fence (a fence would wait for
-    // the copies just issued): each wave first waits for its own copies of
-    // tile it, i.e. until only the 12 copies issued after them (bias it+1,
-    // K/V it+1, bias it+2: 4 each) are outstanding, and LDS reads finish
-    // before a wave reaches the second barrier because their results are
-    // consumed by then.
-    int kv_i = 0, b_i = 0;  // buffers of tile it
+    auto kv_slot = [&](int i) { return kv_buf + i * kKV; };
+    auto b_slot = [&](int i) { return bias_buf + i * (kWaves * kBiasWave); };
+    issue_bias(b_slot(0), j0_of(tile_begin));
+    issue_bias(b_slot(1), j0_of(tile_begin + 1));
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      issue_kv(kv_slot(i), j0_of(tile_begin + i), page_of(j0_of(tile_begin + i)));
+      issue_bias(b_slot(i + 2), j0_of(tile_begin + i + 2));
+    }
+    int page_next = page_of(j0_of(tile_begin + 3));
+    int kv_i = 0, b_i = 0;  // slots of tile it
     for (int it = tile_begin; it < tile_end; ++it) {
-      char* const kv_cur = kv_buf + kv_i * kKV;
-      char* const kv_next = kv_buf + (kv_i ^ 1) * kKV;
-      const int b_n2 = b_i == 0 ? 2 : b_i - 1;  // (b_i + 2) % 3
-      char* const b_cur = bias_buf + b_i * (kWaves * kBiasWave);
-      char* const b_next2 = bias_buf + b_n2 * (kWaves * kBiasWave);
-      issue_kv(kv_next, j0_of(it + 1));
-      issue_bias(b_next2, j0_of(it + 2));
-      wait_vm<12>();
-      lds_barrier();  // tile it is in LDS for every wave
+      wait_vm<10>();
+      lds_barrier();
+      // the page id is used only from here on, so that the wait for its
+      // load comes after the long wait above
+      int page = page_next;
+      asm volatile("" : "+s"(page));
+      issue_kv(kv_slot((kv_i + 3) & 3), j0_of(it + 3), page);
+      issue_bias(b_slot(b_i == 0 ? 5 : b_i - 1), j0_of(it + 5));
       const int j0 = j0_of(it);
-      if (j0 + kKeys > L) zero_v_tail(kv_cur, j0);
-      compute(kv_cur, b_cur, j0);
-      lds_barrier();  // everyone is done with the buffers tiles it+2 / it+3 will reuse
-      kv_i ^= 1;
-      b_i = b_i == 2 ? 0 : b_i + 1;
+      if (j0 + kKeys > L) zero_v_tail(kv_slot(kv_i), j0);
+      compute(kv_slot(kv_i), b_slot(b_i), j0);
+      page_next = page_of(j0_of(it + 4));
+      kv_i = (kv_i + 1) & 3;
+      b_i = b_i == 5 ? 0 : b_i + 1;
     }
     // the last copies re-read tiles nobody uses: let them land before the
     // LDS is released
