@@ -68,15 +68,17 @@ __device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 
 // the compiler does not guard the LDS reads with waits of its own: it cannot
 // tell which LDS bytes such a copy writes, and its conservative waits (for
 // copies into other buffers) would stall the prefetch. Every read of copied
-// data is preceded by an explicit wait_vm<N> and a barrier instead. The
-// statement sets M0 (the copy's LDS base) itself; nothing else in this
-// kernel keeps a value in M0.
+// data is preceded by an explicit wait_vm<N> and a barrier instead (both
+// fenced against compiler reordering), and a copy only writes a slot that
+// no wave reads until then, so the statement needs no memory clobber. It
+// sets M0 (the copy's LDS base) itself; nothing else in this kernel keeps a
+// value in M0.
 __device__ __forceinline__ void dma16(const u32x4_t rsrc, char* lds, uint32_t voff) {
   const uint32_t m0v = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0v), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
+               : "m0");
 #pragma clang diagnostic pop
 }
 
@@ -86,6 +88,20 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// Entry x (16 bits each, x = 0..7) of the result is entry x + s of v, zero
+// where x + s falls outside 0..7.
+__device__ __forceinline__ u32x4_t shift_entries(u32x4_t v, int s) {
+  unsigned __int128 w = (unsigned __int128)v[0] | ((unsigned __int128)v[1] << 32) |
+                        ((unsigned __int128)v[2] << 64) | ((unsigned __int128)v[3] << 96);
+  if (s >= 8 || s <= -8)
+    w = 0;
+  else if (s >= 0)
+    w >>= 16 * s;
+  else
+    w <<= -16 * s;
+  return u32x4_t{(uint32_t)w, (uint32_t)(w >> 32), (uint32_t)(w >> 64), (uint32_t)(w >> 96)};
 }
 
 __device__ __forceinline__ float lane_swap32_max(float v) {
@@ -234,7 +250,10 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   // bytes, so instruction u writes 1 KB in lane order (lane = 32h + n): each
   // lane copies for its own column n.
   // Copies read through one resource over the wave's rows plus 64 entries
-  // on each side (inside the tensor); pieces outside it read as zeros.
+  // on each side (inside the tensor). A piece is read from its position
+  // clamped into the resource: with E >= 8 a piece moved that way holds an
+  // entry in 0 <= d < E only in the first or last row of the tensor, whose
+  // lanes shift the entries back into place in registers.
   const int E = P.E;
   const int64_t tensor_elems = (int64_t)P.T * P.H * E;
   int64_t reg_lo = 0, reg_hi = 0;
@@ -252,9 +271,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   const u32x4_t rel_rsrc = make_rsrc(rel_base, (uint32_t)((reg_hi - reg_lo) * 2));
   const int64_t my_row_abs = (int64_t)t * P.H + hq;
   const int rel_lane_elem = (int)(my_row_abs * E - reg_lo);  // row start, relative to the resource
-  // Pieces can straddle the resource only at the two ends of the whole
-  // tensor: lanes of the first or last tensor row fix their values in
-  // registers.
+  const int rel_last_piece = (int)(reg_hi - reg_lo) - 8;      // last piece start inside the resource
   const bool edge_row = E > 0 && row_ok && (my_row_abs == 0 || my_row_abs == (int64_t)P.T * P.H - 1);
   // distances covered by a tile over the workgroup's rows: [p_lo - j0 - 31, p_hi - j0]
   const int p_lo = ia + L - S, p_hi = ib + L - S;
@@ -300,7 +317,8 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int e_lo = no_bias ? 0 : p - (j0 + 16 * u + 8 * h) - 7;
-      dma16(rel_rsrc, my_bias + 1024 * u, (uint32_t)(rel_lane_elem + e_lo) * 2u);
+      const int at = min(max(rel_lane_elem + e_lo, 0), rel_last_piece);
+      dma16(rel_rsrc, my_bias + 1024 * u, (uint32_t)at * 2u);
     }
   };
 
@@ -321,7 +339,9 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   // rel_logits. Scores stay unscaled (the scale is positive) until the
   // exponent, so that the scale costs no extra instruction per score.
   const bool edge_wave = __builtin_amdgcn_ballot_w64(edge_row) != 0;
-  auto compute = [&](const char* kv, const char* bias, int j0) {
+  // after_qk and after_exp run once the QK MFMAs, resp. the exponentials,
+  // are issued: the next tiles' copies go there, spread over the stage
+  auto compute = [&](const char* kv, const char* bias, int j0, auto&& after_qk, auto&& after_exp) {
     // S^T = K Q^T (+ bias / scale); register a of lane (h, n) is key j0 + 16h + a
     const int bc = band_class(j0);
     const char* my_bias = bias + wave * kBiasWave;
@@ -340,6 +360,17 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
 #pragma unroll
       for (int u = 0; u < 2; ++u) bb[u] = *reinterpret_cast<const u32x4_t*>(my_bias + 1024 * u + 16 * lane);
       const int e_lo0 = p - (j0 + 8 * h) - 7;
+      if (edge_wave) {
+        asm volatile("");
+        // first and last row of the tensor: a piece read at `at` instead of
+        // `want` has its entries moved back by want - at
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int want = rel_lane_elem + e_lo0 - 16 * u;
+          const int at = min(max(want, 0), rel_last_piece);
+          bb[u] = shift_entries(bb[u], want - at);
+        }
+      }
       if (bc == 2) {
         asm volatile("");
 #pragma unroll
@@ -352,28 +383,12 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
             bb[u][w] &= lo_ok | hi_ok;
           }
       }
-      if (edge_wave) {
-        asm volatile("");
-        // rows at the very start or end of the tensor: re-read their
-        // in-range entries one by one (clamped reads, kept where in range)
-        const uint16_t* rrow = reinterpret_cast<const uint16_t*>(P.rel) + (edge_row ? my_row_abs * E : 0);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            const int d = e_lo0 - 16 * u + x;
-            const bool keep = edge_row && d >= 0 && d < E;
-            const uint32_t v = rrow[keep ? d : 0];
-            const uint32_t w = bb[u][x >> 1];
-            const uint32_t nw = (x & 1) ? ((w & 0xffffu) | (v << 16)) : ((w & 0xffff0000u) | v);
-            bb[u][x >> 1] = keep ? nw : w;
-          }
-      }
 #pragma unroll
       for (int u = 0; u < 2; ++u)
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, bias_sel[u]),
                                                     __builtin_bit_cast(bf16x8v_t, bb[u]), s, 0, 0, 0);
     }
+    after_qk();
     // masks, then the row max of the unscaled scores, scaled (log2 units)
     const bool interior = (j0 >= lo_max) && (j0 + kKeys <= hi_min);
     if (!interior) {
@@ -405,6 +420,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
       s[a] = e;
       l_part += e;
     }
+    after_exp();
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const u32x4_t pb = {pack_bf16x2(s[8 * kb + 0], s[8 * kb + 1]), pack_bf16x2(s[8 * kb + 2], s[8 * kb + 3]),
@@ -472,11 +488,11 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
       // load comes after the long wait above
       int page = page_next;
       asm volatile("" : "+s"(page));
-      issue_kv(kv_slot((kv_i + 3) & 3), j0_of(it + 3), page);
-      issue_bias(b_slot(b_i == 0 ? 5 : b_i - 1), j0_of(it + 5));
       const int j0 = j0_of(it);
       if (j0 + kKeys > L) zero_v_tail(kv_slot(kv_i), j0);
-      compute(kv_slot(kv_i), b_slot(b_i), j0);
+      compute(
+          kv_slot(kv_i), b_slot(b_i), j0, [&] { issue_kv(kv_slot((kv_i + 3) & 3), j0_of(it + 3), page); },
+          [&] { issue_bias(b_slot(b_i == 0 ? 5 : b_i - 1), j0_of(it + 5)); });
       page_next = page_of(j0_of(it + 4));
       kv_i = (kv_i + 1) & 3;
       b_i = b_i == 5 ? 0 : b_i + 1;
@@ -523,7 +539,8 @@ bool prefill_supported(const AttnParams& P, int dtype_bf16, int head_dim) {
   // than 2 GB (E * H * (32/G + 2) entries)
   const int64_t span = (int64_t)P.E * P.H * (32 / P.G + 2) * 2 + 256;
   // the scores stay unscaled until the exponent: the scale must be positive
-  return dtype_bf16 && head_dim == kD && P.bs_log2 >= 4 && span < 0x7fffffff && P.scale_log2 > 0.f;
+  return dtype_bf16 && head_dim == kD && P.bs_log2 >= 4 && span < 0x7fffffff && P.scale_log2 > 0.f &&
+         (P.E == 0 || P.E >= 8);
 }
 
 int launch_prefill(const AttnParams& P, hipStream_t stream) {

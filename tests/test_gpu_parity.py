@@ -114,6 +114,12 @@ EDGE = [
     dict(name="decode_b80_mixed_lengths", query_lens=[1] * 76 + [2, 3, 1, 4],
          kv_lens=[(37 * i) % 700 + 1 for i in range(80)], num_heads=16, num_kv_heads=4, head_dim=128,
          block_size=16, rel_extent=64),
+    dict(name="prefill_edge_rows_e8", query_lens=[40, 33], kv_lens=[40, 100], num_heads=8, num_kv_heads=2,
+         head_dim=128, block_size=16, rel_extent=8),
+    dict(name="prefill_edge_rows_e13_g8", query_lens=[25, 64], kv_lens=[25, 64], num_heads=16, num_kv_heads=2,
+         head_dim=128, block_size=16, rel_extent=13),
+    dict(name="prefill_extent_5", query_lens=[30], kv_lens=[50], num_heads=8, num_kv_heads=2,
+         head_dim=128, block_size=16, rel_extent=5),
     dict(name="fp32_noncausal_g4", query_lens=[1, 7], kv_lens=[90, 7], num_heads=8, num_kv_heads=2,
          head_dim=64, block_size=8, rel_extent=5, causal=False, dtype=torch.float32),
 ]
