@@ -4,21 +4,24 @@
 // A workgroup (8 waves) owns 256 packed rows of one (request, KV head): row
 // r is token r / G and query head kv_head * G + r % G, so the G query heads
 // that share a KV head share every K/V tile. Wave w owns rows 32w..32w+31
-// as the 32 columns of S^T = K Q^T. Per 64-key tile:
-//   * buffer-to-LDS loads copy the K/V tile (shared by the workgroup) and
-//     each wave's slice of relative bias into LDS, double buffered, one tile
-//     ahead of the arithmetic;
-//   * K rows are stored permuted inside each 32-key half: LDS row
+// as the 32 columns of S^T = K Q^T. Per 64-key tile (two 32-key sub-tiles):
+//   * buffer-to-LDS copies bring the K/V tile (shared by the workgroup, one
+//     tile ahead) and each wave's slice of relative bias (two tiles ahead)
+//     into rings in LDS; a K/V copy names its page by a scalar offset into
+//     one resource per cache;
+//   * K rows are stored permuted inside each sub-tile: LDS row
 //     m = 8i + 4h + k holds key 16h + 4i + k, so that output register a of
 //     lane (h, n) of v_mfma_f32_32x32x16_bf16 is key 16h + a;
 //   * the relative bias is added by the matrix cores too: two more MFMAs per
-//     32-key half multiply a constant 0 / (1/scale) selection matrix by the
+//     sub-tile multiply a constant 0 / (1/scale) selection matrix by the
 //     bias as the B operand, whose 8 k slots per lane are 8 consecutive
-//     entries of one rel_logits row (one unaligned 16-byte copy each, into
-//     aligned LDS slots), so the bias costs no vector-ALU work per score;
+//     entries of one rel_logits row (16-byte pieces of 64-byte runs per row,
+//     copied into aligned LDS slots), so the bias costs no vector-ALU work
+//     per score;
 //   * V^T operands come from the row-major V tile through the LDS transpose
 //     read (lane (g, i) of a 16-lane group receives V[4g + k][col0 + i]);
-//     O^T += V^T P^T takes the S^T registers as its B operand directly;
+//     O^T += V^T P^T takes the probabilities, packed to bf16, as its B
+//     operand;
 //   * softmax in the S^T layout: each query column lives in two lanes
 //     (l and l ^ 32), so a row max or sum is one lane swap.
 // Chunks of every K/V row in LDS are XOR-swizzled so that the K operand
@@ -30,6 +33,8 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace relattn {
 
 namespace {
@@ -37,13 +42,16 @@ namespace {
 constexpr int kD = 128;
 constexpr int kWaves = 8;
 constexpr int kRowsWG = 32 * kWaves;  // packed query rows per workgroup
-constexpr int kKeys = 32;             // keys per tile
+constexpr int kKeys = 64;             // keys per tile (one stage of the key loop)
+constexpr int kSub = 32;              // keys per MFMA sub-tile
 constexpr int kRowBytes = kD * 2;
-constexpr int kHalf = kKeys * kRowBytes;  // K (or V) part of a tile: 8 KB
-constexpr int kKV = 2 * kHalf;            // 16 KB
-constexpr int kBiasWave = 32 * kKeys * 2;  // one wave's bias slice of a tile: 2 KB
-constexpr int kKvSlots = 4;               // K/V ring: copies 3 tiles ahead
-constexpr int kBiasSlots = 6;             // bias ring: copies 5 tiles ahead
+constexpr int kSubBytes = kSub * kRowBytes;  // K (or V) rows of a sub-tile: 8 KB
+constexpr int kHalf = kKeys * kRowBytes;     // K (or V) part of a tile: 16 KB
+constexpr int kKV = 2 * kHalf;               // 32 KB
+constexpr int kBiasSub = 32 * kSub * 2;      // one wave's bias slice of a sub-tile: 2 KB
+constexpr int kBiasWave = 2 * kBiasSub;      // ... of a tile: 4 KB
+constexpr int kKvSlots = 2;                  // K/V ring: copies 1 tile ahead
+constexpr int kBiasSlots = 3;                // bias ring: copies 2 tiles ahead
 constexpr float kRescaleSlack = 8.0f;     // log2 units, as in the decode kernel
 
 typedef __bf16 bf16x8v_t __attribute__((ext_vector_type(8)));
@@ -82,6 +90,16 @@ __device__ __forceinline__ void dma16(const u32x4_t rsrc, char* lds, uint32_t vo
 #pragma clang diagnostic pop
 }
 
+// the same copy with a scalar byte offset added to every lane's offset
+__device__ __forceinline__ void dma16_soff(const u32x4_t rsrc, char* lds, uint32_t voff, uint32_t soff) {
+  const uint32_t m0v = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0v), "v"(voff), "s"(rsrc), "s"(soff)
+               : "m0");
+#pragma clang diagnostic pop
+}
+
 // workgroup execution barrier without a memory fence; the empty asm keeps the
 // compiler from moving memory operations across it
 __device__ __forceinline__ void lds_barrier() {
@@ -104,6 +122,13 @@ __device__ __forceinline__ u32x4_t shift_entries(u32x4_t v, int s) {
   return u32x4_t{(uint32_t)w, (uint32_t)(w >> 32), (uint32_t)(w >> 64), (uint32_t)(w >> 96)};
 }
 
+// c + the two bf16 halves of w (v_dot2_f32_bf16 against (1, 1))
+__device__ __forceinline__ float dot2_bf16_ones(uint32_t w, float c) {
+  typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+  const bf16x2v_t one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w), one, c, false);
+}
+
 __device__ __forceinline__ float lane_swap32_max(float v) {
   const uint32_t u = __float_as_uint(v);
   auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
@@ -118,6 +143,9 @@ __device__ __forceinline__ float lane_swap32_sum(float v) {
 // block_table is passed again as a restrict-qualified argument so that page
 // lookups compile to scalar loads (a vector load would make the next wait for
 // it also wait for the copies in flight)
+// kWide: a cache spans 4 GB or more, so that K/V copies build a resource
+// per page instead of passing a 32-bit offset
+template <bool kWide>
 __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
                                                                  const int32_t* __restrict__ block_table) {
   // the K/V ring, then the bias ring (160 KB)
@@ -202,8 +230,8 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
     const int vrow = key + (lane >> 4);
     k_src = (uint32_t)(lane >> 4) * row_bytes + 16u * (uint32_t)((lane & 15) ^ swz(krow));
     v_src = (uint32_t)(lane >> 4) * row_bytes + 16u * (uint32_t)((lane & 15) ^ swz(vrow));
-    k_dst = krow0 * kRowBytes;
-    v_dst = kHalf + key * kRowBytes;
+    k_dst = krow0 * kRowBytes;          // + kSubBytes * sub-tile
+    v_dst = kHalf + key * kRowBytes;    // + kSubBytes * sub-tile
   }
   // K operand read of step kk: row n, logical chunk 2kk + h; the
   // chunk is (2kk) ^ (h ^ swz(n)) as 2kk and h occupy disjoint bits
@@ -232,23 +260,28 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   const int bs_mask = P.bs - 1;
   const int32_t* __restrict__ bt_row = block_table + (int64_t)b * P.max_blocks;
   const int last_page = ((L > 0 ? L : 1) - 1) >> bs_log2;
-  // raw page-table entry of this wave's keys of the tile at j0 (a scalar
-  // load; keys past L map to the request's last page)
+  // raw page-table entry of this wave's keys of the sub-tile at j0 (a
+  // scalar load; keys past L map to the request's last page)
   auto page_of = [&](int j0) -> int {
     int pidx = (j0 + 4 * wave) >> bs_log2;
     pidx = pidx > last_page ? last_page : pidx;
     return bt_row[pidx];
   };
+  // caches under 4 GB: one resource each, a copy passes its page's offset
+  // as the scalar offset
+  const u32x4_t k_rsrc = make_rsrc(P.k, 0xffffffffu);
+  const u32x4_t v_rsrc = make_rsrc(P.v, 0xffffffffu);
   const char* kbytes = reinterpret_cast<const char*>(P.k);
   const char* vbytes = reinterpret_cast<const char*>(P.v);
   const int64_t head_bytes = (int64_t)g * kD * 2;
 
   // ---- relative-bias copy geometry ----
-  // The wave's slice of a tile: for each (part u, lane half h) the 8 entries
-  // d = p - (j0 + 16u + 8h) - 7 .. +7 of each of its 32 rows, i.e. the bias
-  // of keys 16u + 8h + 7 - x for entry x. LDS layout [u][h][row n] x 16
-  // bytes, so instruction u writes 1 KB in lane order (lane = 32h + n): each
-  // lane copies for its own column n.
+  // The wave's slice of a tile is, for each of its 32 rows, the 32 entries
+  // d = p - j0 - 31 .. p - j0 (64 contiguous bytes) as four 16-byte pieces:
+  // piece q holds d = p - j0 - 31 + 8q .. +7, i.e. the bias of keys
+  // 16u + 8h + 7 - x for entry x with q = 3 - 2u - h. Copy instruction k
+  // moves rows 16k .. 16k + 15 whole (lane l: row 16k + l % 16, piece l / 16),
+  // so that it reads 16 runs of 64 bytes; its 1 KB lands in lane order.
   // Copies read through one resource over the wave's rows plus 64 entries
   // on each side (inside the tensor). A piece is read from its position
   // clamped into the resource: with E >= 8 a piece moved that way holds an
@@ -272,13 +305,27 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   const int64_t my_row_abs = (int64_t)t * P.H + hq;
   const int rel_lane_elem = (int)(my_row_abs * E - reg_lo);  // row start, relative to the resource
   const int rel_last_piece = (int)(reg_hi - reg_lo) - 8;      // last piece start inside the resource
+  // the rows this lane copies (k = 0, 1): first entry of piece 0 of the
+  // tile at key 0, relative to the resource
+  int cp_elem[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int rc = min(r0 + 32 * wave + 16 * k + (lane & 15), nrows - 1);
+    const int itok_c = rc / G;
+    const int64_t row_abs_c = (int64_t)(t0 + itok_c) * P.H + g * G + rc % G;
+    cp_elem[k] = (int)(row_abs_c * E - reg_lo) + (itok_c + L - S) - 31 + 8 * (lane >> 4);
+  }
+  // where lane (h, n) finds its piece u of its row
+  uint32_t bias_rd[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) bias_rd[u] = (uint32_t)(1024 * (n >> 4) + 16 * ((n & 15) + 16 * (3 - 2 * u - h)));
   const bool edge_row = E > 0 && row_ok && (my_row_abs == 0 || my_row_abs == (int64_t)P.T * P.H - 1);
   // distances covered by a tile over the workgroup's rows: [p_lo - j0 - 31, p_hi - j0]
   const int p_lo = ia + L - S, p_hi = ib + L - S;
-  // 0: no key of the tile gets a bias, 1: every score does, 2: some do
+  // sub-tile at j0 -> 0: no key gets a bias, 1: every score does, 2: some do
   auto band_class = [&](int j0) -> int {
-    if (E == 0 || p_hi - j0 < 0 || p_lo - (j0 + kKeys - 1) >= E) return 0;
-    if (p_lo - (j0 + kKeys - 1) >= 0 && p_hi - j0 < E) return 1;
+    if (E == 0 || p_hi - j0 < 0 || p_lo - (j0 + kSub - 1) >= E) return 0;
+    if (p_lo - (j0 + kSub - 1) >= 0 && p_hi - j0 < E) return 1;
     return 2;
   };
   // A operand of the bias MFMAs: lane (h', m) holds row m (key sigma(m)) and
@@ -301,24 +348,30 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
     }
   }
 
-  auto issue_kv = [&](char* kv, int j0, int page) {
+  // K/V copies of sub-tile j of the tile in kv, keys from j0 (its first key)
+  auto issue_kv = [&](char* kv, int j, int j0, int page) {
     page = page < 0 ? 0 : (page >= P.num_blocks ? P.num_blocks - 1 : page);
     page = __builtin_amdgcn_readfirstlane(page);
     const int key0 = j0 + 4 * wave;
-    const int64_t base = (((int64_t)page << bs_log2) + (key0 & bs_mask)) * row_bytes + head_bytes;
-    dma16(make_rsrc(kbytes + base, 0x7fffffffu), kv + k_dst, k_src);
-    dma16(make_rsrc(vbytes + base, 0x7fffffffu), kv + v_dst, v_src);
+    if constexpr (kWide) {
+      const int64_t base = (((int64_t)page << bs_log2) + (key0 & bs_mask)) * row_bytes + head_bytes;
+      dma16(make_rsrc(kbytes + base, 0x7fffffffu), kv + kSubBytes * j + k_dst, k_src);
+      dma16(make_rsrc(vbytes + base, 0x7fffffffu), kv + kSubBytes * j + v_dst, v_src);
+    } else {
+      const uint32_t off = (((uint32_t)page << bs_log2) + (uint32_t)(key0 & bs_mask)) * row_bytes + (uint32_t)head_bytes;
+      dma16_soff(k_rsrc, kv + kSubBytes * j + k_dst, k_src, off);
+      dma16_soff(v_rsrc, kv + kSubBytes * j + v_dst, v_src, off);
+    }
   };
-  auto issue_bias = [&](char* bias, int j0) {
-    char* my_bias = bias + wave * kBiasWave;
+  // bias copies of the sub-tile at j0 into bias (the wave's slice)
+  auto issue_bias = [&](char* my_bias, int j0) {
     // a tile that no bias reaches re-reads the row's first entries (cached),
     // so that it costs no HBM traffic
     const bool no_bias = band_class(j0) == 0;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int e_lo = no_bias ? 0 : p - (j0 + 16 * u + 8 * h) - 7;
-      const int at = min(max(rel_lane_elem + e_lo, 0), rel_last_piece);
-      dma16(rel_rsrc, my_bias + 1024 * u, (uint32_t)at * 2u);
+    for (int k = 0; k < 2; ++k) {
+      const int at = no_bias ? 0 : min(max(cp_elem[k] - j0, 0), rel_last_piece);
+      dma16(rel_rsrc, my_bias + 1024 * k, (uint32_t)at * 2u);
     }
   };
 
@@ -330,22 +383,10 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   float m_ref = kNegInf;  // running reference max of the column (log2 units)
   float l_part = 0.f;     // this lane's share of the column sum
   const float scale_log2 = P.scale_log2;  // scores are acc * scale_log2 (bias included)
-
-  // One tile. Masks are applied in branches that keep their computation
-  // inside (the empty asm statements stop the compiler from turning them
-  // into selects computed on every tile): score masks only on tiles some row
-  // does not see whole, bias masks only where the band covers part of the
-  // tile, the edge-row patch only in waves holding the first or last row of
-  // rel_logits. Scores stay unscaled (the scale is positive) until the
-  // exponent, so that the scale costs no extra instruction per score.
   const bool edge_wave = __builtin_amdgcn_ballot_w64(edge_row) != 0;
-  // after_qk and after_exp run once the QK MFMAs, resp. the exponentials,
-  // are issued: the next tiles' copies go there, spread over the stage
-  auto compute = [&](const char* kv, const char* bias, int j0, auto&& after_qk, auto&& after_exp) {
-    // S^T = K Q^T (+ bias / scale); register a of lane (h, n) is key j0 + 16h + a
-    const int bc = band_class(j0);
-    const char* my_bias = bias + wave * kBiasWave;
-    f32x16_t s;
+
+  // S^T = K Q^T for the tile in kv: register a of lane (h, n) is key j0 + 16h + a
+  auto qk = [&](const char* kv, f32x16_t& s) {
 #pragma unroll
     for (int a = 0; a < 16; ++a) s[a] = 0.f;
 #pragma unroll
@@ -354,102 +395,96 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, kf),
                                                   __builtin_bit_cast(bf16x8v_t, qreg[kk]), s, 0, 0, 0);
     }
-    if (bc != 0) {
-      // piece u: entry x is distance e_lo0 - 16u + x (key 16u + 8h + 7 - x)
-      u32x4_t bb[2];
+  };
+  // + bias / scale, by two more MFMAs when the band reaches the tile. The
+  // masks sit in branches whose empty asm statements keep their computation
+  // inside (no selects computed on every tile): band masks only where the
+  // band covers part of the tile, the shift only in waves holding the first
+  // or last row of rel_logits.
+  auto add_bias = [&](const char* my_bias, int j0, f32x16_t& s) {
+    const int bc = band_class(j0);
+    if (bc == 0) return;
+    // piece u: entry x is distance e_lo0 - 16u + x (key 16u + 8h + 7 - x)
+    u32x4_t bb[2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) bb[u] = *reinterpret_cast<const u32x4_t*>(my_bias + 1024 * u + 16 * lane);
-      const int e_lo0 = p - (j0 + 8 * h) - 7;
-      if (edge_wave) {
-        asm volatile("");
-        // first and last row of the tensor: a piece read at `at` instead of
-        // `want` has its entries moved back by want - at
+    for (int u = 0; u < 2; ++u) bb[u] = *reinterpret_cast<const u32x4_t*>(my_bias + bias_rd[u]);
+    const int e_lo0 = p - (j0 + 8 * h) - 7;
+    if (edge_wave) {
+      asm volatile("");
+      // first and last row of the tensor: a piece read at `at` instead of
+      // `want` has its entries moved back by want - at
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int want = rel_lane_elem + e_lo0 - 16 * u;
-          const int at = min(max(want, 0), rel_last_piece);
-          bb[u] = shift_entries(bb[u], want - at);
-        }
+      for (int u = 0; u < 2; ++u) {
+        const int want = rel_lane_elem + e_lo0 - 16 * u;
+        const int at = min(max(want, 0), rel_last_piece);
+        bb[u] = shift_entries(bb[u], want - at);
       }
-      if (bc == 2) {
-        asm volatile("");
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const int e = e_lo0 - 16 * u + 2 * w;
-            const uint32_t lo_ok = (uint32_t)e < (uint32_t)E ? 0xffffu : 0u;
-            const uint32_t hi_ok = (uint32_t)(e + 1) < (uint32_t)E ? 0xffff0000u : 0u;
-            bb[u][w] &= lo_ok | hi_ok;
-          }
-      }
+    }
+    if (bc == 2) {
+      asm volatile("");
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, bias_sel[u]),
-                                                    __builtin_bit_cast(bf16x8v_t, bb[u]), s, 0, 0, 0);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int e = e_lo0 - 16 * u + 2 * w;
+          const uint32_t lo_ok = (uint32_t)e < (uint32_t)E ? 0xffffu : 0u;
+          const uint32_t hi_ok = (uint32_t)(e + 1) < (uint32_t)E ? 0xffff0000u : 0u;
+          bb[u][w] &= lo_ok | hi_ok;
+        }
     }
-    after_qk();
-    // masks, then the row max of the unscaled scores, scaled (log2 units)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, bias_sel[u]),
+                                                  __builtin_bit_cast(bf16x8v_t, bb[u]), s, 0, 0, 0);
+  };
+  // scores of keys a row does not see -> -inf (only on tiles some row does
+  // not see whole)
+  auto mask_scores = [&](int j0, f32x16_t* s) {
     const bool interior = (j0 >= lo_max) && (j0 + kKeys <= hi_min);
     if (!interior) {
       asm volatile("");
-      // visible registers: row_lo - jb <= a < row_hi - jb
-      const int jb = j0 + 16 * h;
-      const int a_lo = row_lo - jb, a_hi = row_hi - jb;
+      // visible registers of sub-tile j: row_lo - jb <= a < row_hi - jb
 #pragma unroll
-      for (int a = 0; a < 16; ++a) s[a] = (a >= a_lo && a < a_hi) ? s[a] : kNegInf;
+      for (int j = 0; j < 2; ++j) {
+        const int jb = j0 + kSub * j + 16 * h;
+        const int a_lo = row_lo - jb, a_hi = row_hi - jb;
+#pragma unroll
+        for (int a = 0; a < 16; ++a) s[j][a] = (a >= a_lo && a < a_hi) ? s[j][a] : kNegInf;
+      }
     }
-    float mx = kNegInf;
+  };
+  // O^T += V^T P^T for sub-tile j of the tile in kv; pb holds P^T (bf16) as
+  // the B operand: block kb is registers 8kb..8kb+7 of the sub-tile's scores
+  auto pv = [&](const char* kv, int j, const u32x4_t* pb) {
 #pragma unroll
-    for (int a = 0; a < 16; ++a) mx = fmaxf(mx, s[a]);
-    mx = row_ok ? mx * scale_log2 : kNegInf;
-    mx = lane_swap32_max(mx);
-    if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleSlack) != 0) {
-      const float m_new = fmaxf(m_ref, mx);
-      const float alpha = m_ref == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-      m_ref = m_new;
-      l_part *= alpha;
-#pragma unroll
-      for (int mt = 0; mt < kD / 32; ++mt) oacc[mt] *= alpha;
-    }
-    const float m_use = m_ref == kNegInf ? 0.f : m_ref;
-    // probabilities as the B operand of PV: block kb takes registers 8kb..8kb+7
-#pragma unroll
-    for (int a = 0; a < 16; ++a) {
-      const float e = __builtin_amdgcn_exp2f(fmaf(s[a], scale_log2, -m_use));
-      s[a] = e;
-      l_part += e;
-    }
-    after_exp();
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const u32x4_t pb = {pack_bf16x2(s[8 * kb + 0], s[8 * kb + 1]), pack_bf16x2(s[8 * kb + 2], s[8 * kb + 3]),
-                          pack_bf16x2(s[8 * kb + 4], s[8 * kb + 5]), pack_bf16x2(s[8 * kb + 6], s[8 * kb + 7])};
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int mt = 0; mt < kD / 32; ++mt) {
         u32x2_t part[2];
 #pragma unroll
         for (int sr = 0; sr < 2; ++sr) {
           const int c = kb | ((mt & 1) << 1) | ((((mt >> 1) ^ sr) & 1) << 2);
-          const char* addr = kv + kHalf + (8 * kb + 4 * sr) * kRowBytes + v_rd[c];
+          const char* addr = kv + kHalf + kSubBytes * j + (8 * kb + 4 * sr) * kRowBytes + v_rd[c];
           part[sr] = __builtin_bit_cast(
               u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)addr));
         }
         const u32x4_t av = {part[0][0], part[0][1], part[1][0], part[1][1]};
         oacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, av),
-                                                           __builtin_bit_cast(bf16x8v_t, pb), oacc[mt], 0, 0, 0);
+                                                           __builtin_bit_cast(bf16x8v_t, pb[kb]), oacc[mt], 0, 0, 0);
       }
-    }
   };
 
   // The tile holding key L - 1 may hold keys past L, whose V rows may be
   // anything (NaN) while their probabilities are 0 (0 * NaN = NaN): once it
   // is in LDS the workgroup overwrites those rows with zeros. Thread i
-  // clears 16 bytes of row i/16.
+  // clears 16 bytes of rows i/16 and 32 + i/16.
   auto zero_v_tail = [&](char* kv, int j0) {
-    const int r_from = L - j0;  // rows r_from .. 31 hold keys past L
-    const int r = threadIdx.x >> 4;
-    if (r >= r_from) *reinterpret_cast<u32x4_t*>(kv + kHalf + r * kRowBytes + 16 * (threadIdx.x & 15)) = u32x4_t{0u, 0u, 0u, 0u};
+    const int r_from = L - j0;  // rows r_from .. 63 hold keys past L
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int r = (threadIdx.x >> 4) + 32 * rr;
+      if (r >= r_from) *reinterpret_cast<u32x4_t*>(kv + kHalf + r * kRowBytes + 16 * (threadIdx.x & 15)) = u32x4_t{0u, 0u, 0u, 0u};
+    }
     // the stores have landed before the barrier (lgkmcnt(0) only)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
@@ -457,45 +492,94 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   };
 
   // ---- key loop ----
-  // Rings in LDS: K/V tiles are copied 3 tiles ahead (4 slots), bias slices
-  // 5 tiles ahead (6 slots; the bias stream has no reuse and comes from
-  // HBM); page ids are loaded a stage before the copy that uses them. A
-  // stage waits for the wave's own copies of tile it, i.e. until only the 10
-  // copies issued after them are outstanding (bias it+2, then K/V and bias of
-  // tiles it+1 / it+3 and it+2 / it+4: 2 each), then meets the other waves at
+  // Rings in LDS: the K/V tile is copied one tile ahead (2 slots), the bias
+  // slices two tiles ahead (3 slots; the bias stream has no reuse and comes
+  // from HBM); page ids are loaded a stage before the copy that uses them.
+  // Stage s waits for the wave's own copies of tile s, i.e. until only the 4
+  // bias copies of tile s + 1 are outstanding, then meets the other waves at
   // a barrier without a memory fence (a fence would wait for every copy in
-  // flight). Past the barrier every wave is done with tile it-1, whose slots
-  // then take tiles it+3 and it+5. Copies past the last tile re-read it, so
-  // that every stage issues the same copies.
+  // flight). Past the barrier every wave is done with tile s - 1, whose
+  // slots then take the K/V of tile s + 1 and the bias of tile s + 2. Copies
+  // past the last tile re-read it, so that every stage issues the same
+  // copies.
   if (tile_begin < tile_end) {
-    const int last = tile_end - 1;
+    const int tb = tile_begin, te = tile_end;
+    const int last = te - 1;
     auto j0_of = [&](int it) { return kstart + kKeys * min(it, last); };
     auto kv_slot = [&](int i) { return kv_buf + i * kKV; };
-    auto b_slot = [&](int i) { return bias_buf + i * (kWaves * kBiasWave); };
-    issue_bias(b_slot(0), j0_of(tile_begin));
-    issue_bias(b_slot(1), j0_of(tile_begin + 1));
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      issue_kv(kv_slot(i), j0_of(tile_begin + i), page_of(j0_of(tile_begin + i)));
-      issue_bias(b_slot(i + 2), j0_of(tile_begin + i + 2));
-    }
-    int page_next = page_of(j0_of(tile_begin + 3));
-    int kv_i = 0, b_i = 0;  // slots of tile it
-    for (int it = tile_begin; it < tile_end; ++it) {
-      wait_vm<10>();
+    auto b_slot = [&](int i) { return bias_buf + i * (kWaves * kBiasWave) + wave * kBiasWave; };
+    auto issue_bias_tile = [&](int slot, int j0) {
+      issue_bias(b_slot(slot), j0);
+      issue_bias(b_slot(slot) + kBiasSub, j0 + kSub);
+    };
+    // copies of the stages before tb: bias tb, K/V tb, bias tb + 1
+    issue_bias_tile(0, j0_of(tb));
+    issue_kv(kv_slot(0), 0, j0_of(tb), page_of(j0_of(tb)));
+    issue_kv(kv_slot(0), 1, j0_of(tb) + kSub, page_of(j0_of(tb) + kSub));
+    issue_bias_tile(1, j0_of(tb + 1));
+    int page_next0 = page_of(j0_of(tb + 1)), page_next1 = page_of(j0_of(tb + 1) + kSub);
+    int kv_i = 0, b_i = 0;  // slots of tile s
+    for (int s = tb; s < te; ++s) {
+      wait_vm<4>();
       lds_barrier();
-      // the page id is used only from here on, so that the wait for its
-      // load comes after the long wait above
-      int page = page_next;
-      asm volatile("" : "+s"(page));
-      const int j0 = j0_of(it);
-      if (j0 + kKeys > L) zero_v_tail(kv_slot(kv_i), j0);
-      compute(
-          kv_slot(kv_i), b_slot(b_i), j0, [&] { issue_kv(kv_slot((kv_i + 3) & 3), j0_of(it + 3), page); },
-          [&] { issue_bias(b_slot(b_i == 0 ? 5 : b_i - 1), j0_of(it + 5)); });
-      page_next = page_of(j0_of(it + 4));
-      kv_i = (kv_i + 1) & 3;
-      b_i = b_i == 5 ? 0 : b_i + 1;
+      // the page ids are used only from here on, so that the wait for
+      // their loads comes after the long wait above
+      int page0 = page_next0, page1 = page_next1;
+      asm volatile("" : "+s"(page0), "+s"(page1));
+      const int j0 = j0_of(s);
+      const int jn = j0_of(s + 1);
+      issue_kv(kv_slot(kv_i ^ 1), 0, jn, page0);
+      issue_kv(kv_slot(kv_i ^ 1), 1, jn + kSub, page1);
+      const int b_n = b_i == 0 ? 2 : b_i - 1;  // slot of tile s - 1 = slot of tile s + 2
+      issue_bias_tile(b_n, j0_of(s + 2));
+      page_next0 = page_of(j0_of(s + 2));
+      page_next1 = page_of(j0_of(s + 2) + kSub);
+      char* kv = kv_slot(kv_i);
+      if (j0 + kKeys > L) zero_v_tail(kv, j0);
+      // S^T = K Q^T (+ bias / scale) of the two sub-tiles
+      f32x16_t sc[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        qk(kv + kSubBytes * j, sc[j]);
+        add_bias(b_slot(b_i) + kBiasSub * j, j0 + kSub * j, sc[j]);
+      }
+      mask_scores(j0, sc);
+      // row max of the unscaled scores, scaled (log2 units); a new reference
+      // only when it grows by more than the slack
+      float mx = kNegInf;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) mx = fmaxf(mx, sc[j][a]);
+      mx = row_ok ? mx * scale_log2 : kNegInf;
+      mx = lane_swap32_max(mx);
+      if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleSlack) != 0) {
+        asm volatile("");
+        const float m_new = fmaxf(m_ref, mx);
+        const float alpha = m_ref == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+        m_ref = m_new;
+        l_part *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < kD / 32; ++mt) oacc[mt] *= alpha;
+      }
+      const float m_use = m_ref == kNegInf ? 0.f : m_ref;
+      // probabilities (bf16) and their sum, then O += P V per sub-tile
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        u32x4_t pb[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          float e[8];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) e[x] = __builtin_amdgcn_exp2f(fmaf(sc[j][8 * kb + x], scale_log2, -m_use));
+          pb[kb] = u32x4_t{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]), pack_bf16x2(e[6], e[7])};
+#pragma unroll
+          for (int w = 0; w < 4; ++w) l_part = dot2_bf16_ones(pb[kb][w], l_part);
+        }
+        pv(kv, j, pb);
+      }
+      kv_i ^= 1;
+      b_i = b_i == 2 ? 0 : b_i + 1;
     }
     // the last copies re-read tiles nobody uses: let them land before the
     // LDS is released
@@ -547,7 +631,14 @@ int launch_prefill(const AttnParams& P, hipStream_t stream) {
   const int qtiles = (P.max_q * P.G + kRowsWG - 1) / kRowsWG;
   dim3 grid(qtiles * P.splits, P.Hkv, P.B);
   if (grid.x == 0 || P.B == 0) return 0;
-  hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(kWaves * 64), 0, stream, P, P.block_table);
+  // byte offsets of K/V copies within a cache (a copy reaches up to 4 rows
+  // past its first key's row)
+  const uint64_t row = (uint64_t)P.Hkv * kD * 2;
+  const uint64_t cache_bytes = (uint64_t)P.num_blocks * ((uint64_t)1 << P.bs_log2) * row;
+  if (cache_bytes + 4 * row < ((uint64_t)1 << 32))
+    hipLaunchKernelGGL(attn_prefill_kernel<false>, grid, dim3(kWaves * 64), 0, stream, P, P.block_table);
+  else
+    hipLaunchKernelGGL(attn_prefill_kernel<true>, grid, dim3(kWaves * 64), 0, stream, P, P.block_table);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -218,3 +218,31 @@ def test_requests_without_keys_give_zeros(splits, dtype):
     ref = oracle.oracle_attention(**ref_kw)
     compare(out, ref, case.dtype, what=f"no keys splits={splits}")
     assert torch.count_nonzero(out[:21]) == 0
+
+
+def test_cache_over_4gb():
+    """K/V caches past 4 GB (the prefill kernel's per-page resources): the
+    pages of a small case are placed at the far end of a 4.6 GB pool."""
+    case = make_case(name="wide_cache", query_lens=[100, 1, 70], kv_lens=[300, 90, 70], num_heads=16,
+                     num_kv_heads=8, head_dim=128, block_size=16, rel_extent=64, seed=3)
+    big = 150000  # pages of 32 KB: 4.6 GB per cache
+    kw = device_case(case)
+    bt = case.block_table.clone()
+    used = sorted(set(int(x) for x in bt.flatten().tolist()))
+    remap = {p: big - 1 - 5 * i for i, p in enumerate(used)}
+    bt_big = bt.clone().apply_(lambda x: remap[int(x)])
+    log(f"[parity] wide_cache: {len(used)} pages mapped to {min(remap.values())}..{max(remap.values())} of {big}")
+    for name in ("key_cache", "value_cache"):
+        small = kw[name]
+        pool = torch.empty((big,) + tuple(small.shape[1:]), dtype=small.dtype, device=small.device)
+        src = torch.tensor(used, dtype=torch.int64, device=small.device)
+        dst = torch.tensor([remap[p] for p in used], dtype=torch.int64, device=small.device)
+        pool[dst] = small[src]
+        kw[name] = pool
+    kw["block_table"] = bt_big.to(kw["q"].device)
+    from paged_varlen_attention_gqa_amd import rel_attn_fwd
+
+    got = rel_attn_fwd(**kw)
+    torch.cuda.synchronize()
+    ref = oracle.oracle_attention(**case.kwargs())
+    compare(got, ref, case.dtype, what="wide_cache")
