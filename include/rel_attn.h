@@ -63,6 +63,9 @@ extern "C" {
  *   - other calls: work units (requests x KV heads x 64-row query tiles)
  *     are split until the launch has about 1024 workgroups, keeping at
  *     least 256 keys per split.
+ * A call with one split still spreads a decode-shaped request's keys over
+ * the device: with fewer than 1024 (request, KV head) pairs, the waves of
+ * one workgroup per pair share its key range and merge in LDS.
  *
  * is_local:      non-zero when either window side is >= 0.
  * batch_size:    number of requests (>= 1).

@@ -19,6 +19,14 @@
 // The 16-byte chunks of every LDS row are XOR-swizzled by a function of the
 // row so that both read patterns are free of bank conflicts.
 //
+// Three launches share that per-wave loop: one workgroup per (request,
+// split, group of KV heads); a balanced split of the batch's tiles over one
+// round of workgroups (split calls of at most 64 requests); and, for calls
+// with one split (sliding-window calls get one) and few (request, KV head)
+// pairs, a workgroup per pair whose waves share its key range and merge
+// their partial results in LDS, so that long ranges fill the device without
+// a workspace.
+//
 // Score and bias rule: prhub.com.cn report on vLLM PR #48858, "key source
 // snippets" (score_mod_rel_bias); paged-cache layout and the split count:
 // docs.vllm.ai inkling_fa4_rel_attention / inkling_fa4_num_splits.
@@ -51,6 +59,12 @@ constexpr float kRescaleSlack = 8.0f;
 #endif
 constexpr int kDecodeWaves = REL_ATTN_DECODE_WAVES;
 constexpr int kDecodeRing = REL_ATTN_DECODE_RING;
+// in-workgroup split of one-split calls: waves per (request, KV head), and
+// when it is used (fewer pairs than this, key ranges of at least this many
+// keys: each wave then streams at least 4 tiles)
+constexpr int kWgSplitWaves = 4;
+constexpr int kWgSplitMaxPairs = 1024;
+constexpr int kWgSplitMinKeys = 4 * kWgSplitWaves * 16;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -74,6 +88,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char* lds, ui
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds, 16, voff, 0, 0, kStreamPolicy);
 }
 
+// Where a wave of the in-workgroup split leaves its partial result: its
+// own two ring slots, once its copies have landed (o: 16 columns x 128 dims
+// fp32 in the first, one log2-sum-exp per column in the second).
+struct LdsPartial {
+  float* o;
+  float* lse;
+};
+
 // One wave's work on one piece of one request: the request's rows (S * G
 // <= 16 columns) against KV head g over the keys [c0, c1) (c0 a multiple of
 // 16 inside the request's visible range, c1 its end or a later multiple of
@@ -82,11 +104,11 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char* lds, ui
 // block_table is the same table as P.block_table, restrict-qualified so that
 // page lookups compile to scalar loads: they then count on the scalar/LDS
 // counter and a wait for them never waits for the K/V copies in flight.
-template <int NW, int RING>
+template <int NW, int RING, bool PART = false>
 __device__ __forceinline__ void decode_piece(const AttnParams& P, const int32_t* __restrict__ block_table,
                                              char* ring0, char* ring1, char* ring2, int wave, int lane,
                                              int b, int g, int t0, int S, int L, int c0_in, int c1_in,
-                                             int split) {
+                                             int split, LdsPartial part = {nullptr, nullptr}) {
   const int n = lane & 15;  // column (query row) / K row / transpose-read lane
   const int q = lane >> 4;  // 0..3
   const int G = P.G;
@@ -110,6 +132,10 @@ __device__ __forceinline__ void decode_piece(const AttnParams& P, const int32_t*
     // No visible key: the row's output is zero, and an empty split still
     // tells the combine step that it holds nothing. Lane (n, q) writes dims
     // 32q .. 32q+31 of column n.
+    if constexpr (PART) {
+      if (q == 0) part.lse[n] = kNegInf;
+      return;
+    }
     if (col_ok) {
       if (P.splits == 1) {
         uint16_t* op = reinterpret_cast<uint16_t*>(P.out) + ((int64_t)t * P.H + h) * kD + 32 * q;
@@ -402,6 +428,16 @@ __device__ __forceinline__ void decode_piece(const AttnParams& P, const int32_t*
   // lane (q, n) holds dims 16mb + 4q + i of column n; m_ref is the column's
   // reference max (log2 units), the same in the four lanes of a column
   const float l_col = wave_sum_xor_16_32(l_part);
+  if constexpr (PART) {
+    // the wave's copies (also the ones past its last tile) have landed
+    // before its slots take the partial
+    wait_vm<0>();
+    const float inv = l_col > 0.f ? 1.f / l_col : 0.f;
+#pragma unroll
+    for (int mb = 0; mb < kD / 16; ++mb) *reinterpret_cast<f32x4_t*>(part.o + n * kD + 16 * mb + 4 * q) = oacc[mb] * inv;
+    if (q == 0) part.lse[n] = l_col > 0.f ? m_ref + __log2f(l_col) : kNegInf;
+    return;
+  }
   if (!col_ok) return;
   const float inv = l_col > 0.f ? 1.f / l_col : 0.f;
   if (P.splits == 1) {
@@ -457,6 +493,66 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(AttnParams P,
   const int c0 = kstart + split * P.dec_chunk;
   decode_piece<NW, RING>(P, block_table, ring0, ring1, ring2, wave, lane, b, g, t0, S, L, c0,
                          min(c0 + P.dec_chunk, hi), split);
+}
+
+// Calls with one split and few (request, KV head) pairs: a workgroup per
+// (KV head, request) whose NW waves cut the request's key range into NW
+// pieces of whole tiles, then merge their partials through LDS (the split
+// of the key range happens inside the workgroup, so it needs no workspace).
+template <int NW, int RING>
+__global__ __launch_bounds__(NW * 64) void attn_decode_wg_split_kernel(AttnParams P,
+                                                                       const int32_t* __restrict__ block_table) {
+  __shared__ __attribute__((aligned(1024))) char ring0[NW * kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char ring1[NW * kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char ring2[RING > 2 ? NW * kSlotBytes : 16];
+  static_assert(RING == 2 || RING == 3, "ring depth");
+  static_assert(16 * kD * 4 <= kSlotBytes, "a partial fits in a slot");
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int g = blockIdx.x;
+  const int b = blockIdx.z;
+  int t0, S, L;
+  if (!request_bounds(P, b, t0, S, L)) return;
+  const int rows = S * P.G;
+  if (rows > 16) return;  // handled by the prefill or general kernel
+  int kstart, hi, ntiles;
+  request_keys(P, S, L, kstart, hi, ntiles);
+  const int per = (ntiles + NW - 1) / NW;  // tiles per wave
+  const int c0 = kstart + kTile * min(wave * per, ntiles);
+  const int c1 = min(kstart + kTile * min((wave + 1) * per, ntiles), hi);
+  LdsPartial part = {reinterpret_cast<float*>(ring0 + wave * kSlotBytes),
+                     reinterpret_cast<float*>(ring1 + wave * kSlotBytes)};
+  decode_piece<NW, RING, true>(P, block_table, ring0, ring1, ring2, wave, lane, b, g, t0, S, L, c0,
+                               max(c0, c1), 0, part);
+  __syncthreads();
+  // merge: item i is column i / 32, dims 4 (i % 32) .. + 3
+  for (int it = threadIdx.x; it < rows * 32; it += NW * 64) {
+    const int col = it >> 5;
+    const int d0 = 4 * (it & 31);
+    float lse[NW];
+    float mmax = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      lse[w] = reinterpret_cast<const float*>(ring1 + w * kSlotBytes)[col];
+      mmax = fmaxf(mmax, lse[w]);
+    }
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    if (mmax != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        if (lse[w] == kNegInf) continue;
+        const float wt = __builtin_amdgcn_exp2f(lse[w] - mmax);
+        wsum += wt;
+        acc += wt * *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(ring0 + w * kSlotBytes) + col * kD + d0);
+      }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    const int t = t0 + col / P.G;
+    const int h = g * P.G + col % P.G;
+    uint16_t* op = reinterpret_cast<uint16_t*>(P.out) + ((int64_t)t * P.H + h) * kD + d0;
+    *reinterpret_cast<u32x2_t*>(op) = u32x2_t{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  }
 }
 
 // Balanced split of the whole batch (at most 64 requests, num_splits >= 2):
@@ -607,6 +703,11 @@ int launch_decode(const AttnParams& P, int head_dim, hipStream_t stream) {
     const int per_group = slots / groups > 0 ? slots / groups : 1;
     hipLaunchKernelGGL((attn_decode_balanced_kernel<kDecodeWaves, kDecodeRing>), dim3(per_group, groups),
                        dim3(kDecodeWaves * 64), 0, stream, P, P.block_table);
+  } else if (P.splits == 1 && (int64_t)P.B * P.Hkv < kWgSplitMaxPairs && P.dec_chunk >= kWgSplitMinKeys) {
+    // few (request, KV head) pairs with long key ranges and no workspace:
+    // the key range of a pair is shared by the waves of its workgroup
+    hipLaunchKernelGGL((attn_decode_wg_split_kernel<kWgSplitWaves, 2>), dim3(P.Hkv, 1, P.B),
+                       dim3(kWgSplitWaves * 64), 0, stream, P, P.block_table);
   } else {
     // workgroup: kDecodeWaves neighbouring KV heads of one (request, split)
     hipLaunchKernelGGL((attn_decode_kernel<kDecodeWaves, kDecodeRing>), dim3(groups, P.splits, P.B),

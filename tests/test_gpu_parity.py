@@ -120,6 +120,10 @@ EDGE = [
          head_dim=128, block_size=16, rel_extent=13),
     dict(name="prefill_extent_5", query_lens=[30], kv_lens=[50], num_heads=8, num_kv_heads=2,
          head_dim=128, block_size=16, rel_extent=5),
+    dict(name="decode_window_wg_split", query_lens=[1, 2, 4, 1, 1], kv_lens=[700, 900, 1500, 2000, 40],
+         num_heads=16, num_kv_heads=4, head_dim=128, block_size=16, rel_extent=64, window_size=(300, 0)),
+    dict(name="decode_window_long_g8", query_lens=[1, 1, 2], kv_lens=[9000, 5000, 7000], num_heads=32,
+         num_kv_heads=4, head_dim=128, block_size=64, rel_extent=2048, window_size=(4095, 0)),
     dict(name="fp32_noncausal_g4", query_lens=[1, 7], kv_lens=[90, 7], num_heads=8, num_kv_heads=2,
          head_dim=64, block_size=8, rel_extent=5, causal=False, dtype=torch.float32),
 ]
