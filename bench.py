@@ -60,7 +60,9 @@ DESCRIPTIONS = {
     "tiny_fp32": "tiny fp32 correctness case: 2 requests, query lens 5/17, KV lens 37/70, H=4 Hkv=2 "
                  "D=64 bs=16, rel_extent=32",
 }
-BOUND = {"decode_b64": "hbm", "decode_long_b1": "hbm", "mixed_window": "hbm",
+# the bound of the stage's dominant kernel (mixed_window: the prefill kernel,
+# about 80% of the stage)
+BOUND = {"decode_b64": "hbm", "decode_long_b1": "hbm", "mixed_window": "mfma",
          "prefill_chunked": "mfma", "tiny_fp32": "hbm"}
 
 
@@ -77,8 +79,8 @@ STAGE_SOURCES = {
 STAGE_KERNELS = {
     "decode_b64": "attn_decode_balanced_kernel",
     "decode_long_b1": "attn_decode_balanced_kernel",
-    "prefill_chunked": "attn_decode_kernel (no work: rows > 16) + attn_prefill_kernel",
-    "mixed_window": "attn_decode_kernel + attn_prefill_kernel",
+    "prefill_chunked": "attn_decode_wg_split_kernel (no work: rows > 16) + attn_prefill_kernel",
+    "mixed_window": "attn_decode_wg_split_kernel + attn_prefill_kernel",
     "tiny_fp32": "attn_general_kernel",
 }
 COPY_BYTES = 2 << 30  # the plain copy that calibrates the HBM counters
