@@ -57,12 +57,17 @@ DESCRIPTIONS = {
                     "(KV U[2048,32768]), window (4095,0), H=32 Hkv=4 D=128 bs=16, rel_extent=2048, bf16",
     "decode_long_b1": "batch-1 long-context decode: 1 query over 262144 keys, H=32 Hkv=4 D=128 "
                       "bs=64, rel_extent=8192, bf16, split-KV + LSE combine",
+    "decode_1m_b1_kv4": "batch-1 decode over 1048576 keys, H=32 Hkv=4 D=128 bs=64, rel_extent=8192, bf16, "
+                        "split-KV + LSE combine",
+    "decode_1m_b1_kv8": "batch-1 decode over 1048576 keys, H=32 Hkv=8 D=128 bs=64, rel_extent=8192, bf16, "
+                        "split-KV + LSE combine",
     "tiny_fp32": "tiny fp32 correctness case: 2 requests, query lens 5/17, KV lens 37/70, H=4 Hkv=2 "
                  "D=64 bs=16, rel_extent=32",
 }
 # the bound of the stage's dominant kernel (mixed_window: the prefill kernel,
 # about 80% of the stage)
 BOUND = {"decode_b64": "hbm", "decode_long_b1": "hbm", "mixed_window": "mfma",
+         "decode_1m_b1_kv4": "hbm", "decode_1m_b1_kv8": "hbm",
          "prefill_chunked": "mfma", "tiny_fp32": "hbm"}
 
 
@@ -72,6 +77,8 @@ CSRC = os.path.join(ROOT, "paged_varlen_attention_gqa_amd", "csrc")
 STAGE_SOURCES = {
     "decode_b64": ["attn_decode.hip"],
     "decode_long_b1": ["attn_decode.hip"],
+    "decode_1m_b1_kv4": ["attn_decode.hip"],
+    "decode_1m_b1_kv8": ["attn_decode.hip"],
     "prefill_chunked": ["attn_decode.hip", "attn_prefill.hip"],
     "mixed_window": ["attn_decode.hip", "attn_prefill.hip"],
     "tiny_fp32": ["attn_general.hip"],
@@ -79,6 +86,8 @@ STAGE_SOURCES = {
 STAGE_KERNELS = {
     "decode_b64": "attn_decode_balanced_kernel",
     "decode_long_b1": "attn_decode_balanced_kernel",
+    "decode_1m_b1_kv4": "attn_decode_balanced_kernel",
+    "decode_1m_b1_kv8": "attn_decode_balanced_kernel",
     "prefill_chunked": "attn_decode_wg_split_kernel (no work: rows > 16) + attn_prefill_kernel",
     "mixed_window": "attn_decode_wg_split_kernel + attn_prefill_kernel",
     "tiny_fp32": "attn_general_kernel",

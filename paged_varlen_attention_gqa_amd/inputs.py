@@ -229,7 +229,8 @@ def _uniform_ints(n: int, lo: int, hi: int, seed: int, sub: int = 0) -> list:
 
 # The five named workloads. Sizes are the ones the workloads are quoted at; the
 # `scale` argument shrinks them for quick parity runs (documented per config).
-CONFIG_NAMES = ("tiny_fp32", "decode_b64", "prefill_chunked", "mixed_window", "decode_long_b1")
+CONFIG_NAMES = ("tiny_fp32", "decode_b64", "prefill_chunked", "mixed_window", "decode_long_b1",
+                "decode_1m_b1_kv4", "decode_1m_b1_kv8")
 
 
 def config_spec(name: str, scale: float = 1.0, seed: int = 0) -> dict:
@@ -272,6 +273,15 @@ def config_spec(name: str, scale: float = 1.0, seed: int = 0) -> dict:
                     head_dim=128, block_size=64, rel_extent=sc(8192), causal=True,
                     window_size=(-1, -1), softmax_scale=1.0 / math.sqrt(128), dtype=torch.bfloat16,
                     seed=seed, pool_pages=max(sc(4096), (L + 63) // 64))
+    if name in ("decode_1m_b1_kv4", "decode_1m_b1_kv8"):
+        # batch-1 decode over a million keys, with 4 or 8 KV heads (the page
+        # quotes its split caps per KV-head count and measures to 1M tokens)
+        L = sc(1 << 20, 64)
+        return dict(name=name, query_lens=[1], kv_lens=[L], num_heads=32,
+                    num_kv_heads=4 if name.endswith("kv4") else 8, head_dim=128, block_size=64,
+                    rel_extent=sc(8192), causal=True, window_size=(-1, -1),
+                    softmax_scale=1.0 / math.sqrt(128), dtype=torch.bfloat16, seed=seed,
+                    pool_pages=(L + 63) // 64)
     raise KeyError(name)
 
 

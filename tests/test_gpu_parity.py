@@ -57,6 +57,12 @@ def test_full_decode_long_b1():
     _check(make_config("decode_long_b1"))
 
 
+@pytest.mark.parametrize("name", ["decode_1m_b1_kv4", "decode_1m_b1_kv8"])
+def test_full_decode_1m_b1(name):
+    """Batch-1 decode over 2^20 keys (512 splits), 4 and 8 KV heads."""
+    _check(make_config(name))
+
+
 def test_full_prefill_chunked_sampled():
     case = make_config("prefill_chunked")
     cu = case.cu_seqlens_q.tolist()
