@@ -174,6 +174,30 @@ int rel_attn_fwd_splits(const void* q, const void* key_cache, const void* value_
                         size_t workspace_bytes, size_t* workspace_needed, void* stream);
 
 /*
+ * rel_attn_fwd_lse - rel_attn_fwd that also returns each row's log-sum-exp
+ * (the docs.vllm.ai `inkling_fa4_rel_attention` operation with
+ * return_lse=True): same arguments plus
+ *   lse   [num_tokens][num_heads] float32, device, caller-owned: the natural
+ *         log of sum_j exp(softmax_scale * q.k_j + bias_j) over the row's
+ *         visible keys, -inf for a row with none.
+ * The log-sum-exps come out of the split merge, so the call always runs
+ * split: num_splits 1 is taken as 2, and the workspace (and
+ * *workspace_needed) are those of rel_attn_workspace_bytes(max(num_splits, 2),
+ * ...). Returns what rel_attn_fwd returns; REL_ATTN_EINVAL also for a NULL
+ * lse in a call that launches (not for a workspace query or an empty call).
+ * Asynchronous; allocates nothing.
+ */
+int rel_attn_fwd_lse(const void* q, const void* key_cache, const void* value_cache,
+                     const int32_t* block_table, const int32_t* cache_seqlens,
+                     const int32_t* cu_seqlens_q, const void* rel_logits, void* out, float* lse,
+                     int dtype, int num_tokens, int batch_size, int max_seqlen_q,
+                     int max_blocks_per_seq, int num_heads, int num_kv_heads, int head_dim,
+                     int num_blocks, int block_size, int rel_extent, float softmax_scale,
+                     int causal, int window_left, int window_right, int num_splits,
+                     void* workspace, size_t workspace_bytes, size_t* workspace_needed,
+                     void* stream);
+
+/*
  * rel_attn_combine - merge the per-split partial results that
  * rel_attn_fwd_splits left in `workspace` (layout above) into `out`
  * [num_tokens][num_heads][head_dim] of type dtype:

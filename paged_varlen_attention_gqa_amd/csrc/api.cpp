@@ -122,7 +122,7 @@ int prepare(const void* q, const void* key_cache, const void* value_cache, const
     return REL_ATTN_EINVAL;
   if (rel_extent > 0 && num_tokens > 0 && rel_logits == nullptr) return REL_ATTN_EINVAL;
   if (batch_size > 65535 || num_kv_heads > 65535) return REL_ATTN_EUNSUPPORTED;
-  if (num_splits > 1) {
+  if (num_splits > 1 && need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return REL_ATTN_EWORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return REL_ATTN_EINVAL;
   }
@@ -244,6 +244,30 @@ extern "C" int rel_attn_fwd_splits(const void* q, const void* key_cache, const v
   int rc = prepare(REL_ATTN_ARGS, &P, &launch);
   if (rc != REL_ATTN_OK || !launch) return rc;
   return launch_attention(P, dtype, head_dim, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int rel_attn_fwd_lse(const void* q, const void* key_cache, const void* value_cache,
+                                const int32_t* block_table, const int32_t* cache_seqlens,
+                                const int32_t* cu_seqlens_q, const void* rel_logits, void* out, float* lse,
+                                int dtype, int num_tokens, int batch_size, int max_seqlen_q,
+                                int max_blocks_per_seq, int num_heads, int num_kv_heads, int head_dim,
+                                int num_blocks, int block_size, int rel_extent, float softmax_scale,
+                                int causal, int window_left, int window_right, int num_splits,
+                                void* workspace, size_t workspace_bytes, size_t* workspace_needed,
+                                void* stream) {
+  // the log-sum-exps come out of the split merge: one split runs as two
+  if (num_splits == 1) num_splits = 2;
+  AttnParams P;
+  bool launch = false;
+  int rc = prepare(REL_ATTN_ARGS, &P, &launch);
+  if (rc != REL_ATTN_OK || !launch) return rc;  // error, empty call or workspace query
+  if (lse == nullptr) return REL_ATTN_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  rc = launch_attention(P, dtype, head_dim, s);
+  if (rc != REL_ATTN_OK) return rc;
+  P.lse_out = lse;
+  if (relattn::launch_combine(P, dtype == REL_ATTN_BF16, head_dim, s) != 0) return REL_ATTN_ELAUNCH;
+  return REL_ATTN_OK;
 }
 
 #undef REL_ATTN_ARGS

@@ -62,6 +62,7 @@ __global__ __launch_bounds__(W * 64) void combine_kernel(AttnParams P) {
 #pragma unroll
   for (int w = 0; w < W; ++w) sum += red[w];
   const float inv = sum > 0.f ? 1.f / sum : 0.f;
+  if (P.lse_out != nullptr && threadIdx.x == 0) P.lse_out[row] = sum > 0.f ? mx + __logf(sum) : kNegInf;
 
   // ---- weighted sum of the partial outputs ----
   const int sub = lane / kLanesPerSplit;  // split within a load

@@ -30,6 +30,7 @@ struct AttnParams {
   void* out;                 // [T][H][D]
   float* ws_o;               // [splits][T][H][D]   (splits > 1)
   float* ws_lse;             // [splits][T][H]      (splits > 1)
+  float* lse_out;            // [T][H] natural-log log-sum-exp of each row, or null (combine kernel)
   int T, B, max_q, max_blocks, H, Hkv, G, num_blocks, bs, E;
   float scale_log2;          // softmax_scale * log2(e)
   int causal, wl, wr, splits;

@@ -57,6 +57,8 @@ def load_library() -> ctypes.CDLL:
     lib.rel_attn_fwd.restype = c_int
     lib.rel_attn_fwd_splits.argtypes = lib.rel_attn_fwd.argtypes
     lib.rel_attn_fwd_splits.restype = c_int
+    lib.rel_attn_fwd_lse.argtypes = [c_vp] * 9 + lib.rel_attn_fwd.argtypes[8:]  # + lse after out
+    lib.rel_attn_fwd_lse.restype = c_int
     lib.rel_attn_combine.argtypes = [c_vp, c_size, c_vp] + [c_int] * 5 + [c_vp]
     lib.rel_attn_combine.restype = c_int
     _lib = lib
@@ -99,7 +101,7 @@ def _check_dev(name, t, dtype=None):
 
 def _attention_call(entry: str, q, key_cache, value_cache, *, block_table, cache_seqlens,
                     cu_seqlens_q, max_seqlen_q, softmax_scale, causal, window_size, rel_extent,
-                    rel_logits, num_splits, out, workspace, max_kv_len):
+                    rel_logits, num_splits, out, workspace, max_kv_len, lse=None):
     lib = load_library()
     if q.dtype == torch.bfloat16:
         dt = BF16
@@ -135,7 +137,15 @@ def _attention_call(entry: str, q, key_cache, value_cache, *, block_table, cache
         _check_dev("out", out, q.dtype)
         if out.shape != q.shape:
             raise ValueError("out must have the shape of q")
-    need = rel_attn_workspace_bytes(num_splits, T, H, D)
+    with_lse = entry == "rel_attn_fwd_lse"
+    if with_lse:
+        if lse is None:
+            lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+        else:
+            _check_dev("lse", lse, torch.float32)
+            if tuple(lse.shape) != (T, H):
+                raise ValueError(f"lse must be {(T, H)}, got {tuple(lse.shape)}")
+    need = rel_attn_workspace_bytes(max(num_splits, 2) if with_lse else num_splits, T, H, D)
     if need > 0:
         if workspace is None:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -143,15 +153,18 @@ def _attention_call(entry: str, q, key_cache, value_cache, *, block_table, cache
             _check_dev("workspace", workspace)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     stream = torch.cuda.current_stream(q.device).cuda_stream
+    lse_arg = [_ptr(lse)] if with_lse else []
     rc = getattr(lib, entry)(
         _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(block_table), _ptr(cache_seqlens),
-        _ptr(cu_seqlens_q), _ptr(rel_logits if rel_extent > 0 else None), _ptr(out),
+        _ptr(cu_seqlens_q), _ptr(rel_logits if rel_extent > 0 else None), _ptr(out), *lse_arg,
         dt, T, B, int(max_seqlen_q), block_table.shape[1], H, HKV, D, NB, BS, int(rel_extent),
         float(softmax_scale), int(bool(causal)), wl, wr, int(num_splits),
         _ptr(workspace) if need > 0 else ctypes.c_void_p(0), ws_bytes, None,
         ctypes.c_void_p(stream))
     if rc != 0:
         raise RelAttnError(f"{entry}: {rel_attn_strerror(rc)} (code {rc})")
+    if with_lse:
+        return out, lse, num_splits
     return out, workspace, num_splits
 
 
@@ -160,20 +173,24 @@ def rel_attn_fwd(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Te
                  max_seqlen_q: int, softmax_scale: float, causal: bool, window_size=(-1, -1),
                  rel_extent: int, rel_logits: torch.Tensor | None, num_splits: int | None = None,
                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                 max_kv_len: int | None = None) -> torch.Tensor:
-    """Paged varlen GQA attention with the per-token relative bias; returns ``out``.
+                 max_kv_len: int | None = None, return_lse: bool = False,
+                 lse: torch.Tensor | None = None):
+    """Paged varlen GQA attention with the per-token relative bias; returns ``out``,
+    or ``(out, lse)`` with ``return_lse=True`` (``lse`` (num_tokens, num_heads)
+    float32, natural log, -inf for rows without visible keys; the call then
+    runs split, at least 2 pieces).
 
     ``num_splits=None`` asks :func:`rel_attn_num_splits`, with ``max_kv_len``
     defaulting to the page-table capacity (``block_table.shape[1] *
     block_size``), so no device value is read on the host.
     """
-    out, _, _ = _attention_call(
-        "rel_attn_fwd", q, key_cache, value_cache, block_table=block_table,
-        cache_seqlens=cache_seqlens, cu_seqlens_q=cu_seqlens_q, max_seqlen_q=max_seqlen_q,
-        softmax_scale=softmax_scale, causal=causal, window_size=window_size, rel_extent=rel_extent,
-        rel_logits=rel_logits, num_splits=num_splits, out=out, workspace=workspace,
-        max_kv_len=max_kv_len)
-    return out
+    res, extra, _ = _attention_call(
+        "rel_attn_fwd_lse" if return_lse else "rel_attn_fwd", q, key_cache, value_cache,
+        block_table=block_table, cache_seqlens=cache_seqlens, cu_seqlens_q=cu_seqlens_q,
+        max_seqlen_q=max_seqlen_q, softmax_scale=softmax_scale, causal=causal,
+        window_size=window_size, rel_extent=rel_extent, rel_logits=rel_logits,
+        num_splits=num_splits, out=out, workspace=workspace, max_kv_len=max_kv_len, lse=lse)
+    return (res, extra) if return_lse else res
 
 
 def rel_attn_fwd_splits(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor, *,

@@ -32,7 +32,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert set(names) >= {"rel_attn_fwd", "rel_attn_fwd_splits", "rel_attn_combine",
+    assert set(names) >= {"rel_attn_fwd", "rel_attn_fwd_splits", "rel_attn_fwd_lse", "rel_attn_combine",
                           "rel_attn_num_splits", "rel_attn_workspace_bytes", "rel_attn_strerror"}
     for n in names:
         assert hasattr(lib, n), n
@@ -73,13 +73,14 @@ def test_workspace_bytes(lib):
 def _fwd(lib, entry="rel_attn_fwd", **over):
     a = dict(q=1, k=1, v=1, bt=1, sl=1, cu=1, rel=1, out=1, dtype=1, T=4, B=2, maxq=2, mb=3, H=8,
              Hkv=2, D=128, NB=10, bs=16, E=4, scale=0.1, causal=1, wl=-1, wr=-1, splits=1, ws=None,
-             wsb=0, need=None, stream=None)
+             wsb=0, need=None, stream=None, lse=1)
     a.update(over)
     ptr = lambda x: ctypes.c_void_p(x) if x else ctypes.c_void_p(0)  # noqa: E731
     need = a["need"]
+    lse = [ptr(a["lse"])] if entry == "rel_attn_fwd_lse" else []
     return getattr(lib, entry)(
         ptr(a["q"]), ptr(a["k"]), ptr(a["v"]), ptr(a["bt"]), ptr(a["sl"]), ptr(a["cu"]), ptr(a["rel"]),
-        ptr(a["out"]), a["dtype"], a["T"], a["B"], a["maxq"], a["mb"], a["H"], a["Hkv"], a["D"], a["NB"],
+        ptr(a["out"]), *lse, a["dtype"], a["T"], a["B"], a["maxq"], a["mb"], a["H"], a["Hkv"], a["D"], a["NB"],
         a["bs"], a["E"], a["scale"], a["causal"], a["wl"], a["wr"], a["splits"], ptr(a["ws"]), a["wsb"],
         ctypes.byref(need) if need is not None else None, ptr(a["stream"]))
 
@@ -102,19 +103,29 @@ def _fwd(lib, entry="rel_attn_fwd", **over):
     (dict(splits=4, ws=16, wsb=100), -3),
     (dict(splits=4, ws=17, wsb=1 << 30), -1),  # misaligned workspace
 ])
-@pytest.mark.parametrize("entry", ["rel_attn_fwd", "rel_attn_fwd_splits"])
+@pytest.mark.parametrize("entry", ["rel_attn_fwd", "rel_attn_fwd_splits", "rel_attn_fwd_lse"])
 def test_fwd_rejects_before_launch(lib, entry, over, code):
     assert _fwd(lib, entry, **over) == code
 
 
-@pytest.mark.parametrize("entry", ["rel_attn_fwd", "rel_attn_fwd_splits"])
+def test_fwd_lse_checks(lib):
+    # one split runs as two: the workspace query reports two splits' worth
+    need = ctypes.c_size_t(0)
+    assert _fwd(lib, "rel_attn_fwd_lse", splits=1, need=need) == 0
+    assert need.value == 2 * 4 * 8 * 129 * 4
+    assert _fwd(lib, "rel_attn_fwd_lse", splits=1) == -3  # no workspace
+    assert _fwd(lib, "rel_attn_fwd_lse", splits=4, ws=16, wsb=1 << 30, lse=0) == -1  # NULL lse
+    assert _fwd(lib, "rel_attn_fwd_lse", T=0, B=0, q=0, out=0, lse=0) == 0
+
+
+@pytest.mark.parametrize("entry", ["rel_attn_fwd", "rel_attn_fwd_splits", "rel_attn_fwd_lse"])
 def test_fwd_workspace_query(lib, entry):
     need = ctypes.c_size_t(123)
     assert _fwd(lib, entry, splits=8, need=need) == 0
     assert need.value == 8 * 4 * 8 * 129 * 4
 
 
-@pytest.mark.parametrize("entry", ["rel_attn_fwd", "rel_attn_fwd_splits"])
+@pytest.mark.parametrize("entry", ["rel_attn_fwd", "rel_attn_fwd_splits", "rel_attn_fwd_lse"])
 def test_fwd_empty_call_is_ok(lib, entry):
     assert _fwd(lib, entry, T=0, B=0, q=0, out=0) == 0
 
