@@ -185,6 +185,9 @@ def main():
     ap.add_argument("--config", default="decode_b64", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--num-splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="extra calls after the timed ones, each after a 1 GiB write that flushes the "
+                         "L2 and the 256 MB last-level cache (reported as stage_us_cold_mean)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 2 GiB copy first (for HBM counter runs)")
     args = ap.parse_args()
@@ -246,6 +249,19 @@ def main():
     wall = time.perf_counter() - t0
     stage_ms = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
     ms_per_step = wall * 1e3 / args.steps
+    # the same stage with no input left in the caches: a 1 GiB write before
+    # each call (outside the events, not part of the timed steps)
+    cold_ms = np.array([])
+    if args.cold_steps > 0:
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        cevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.cold_steps)]
+        for ev in cevs:
+            scratch.fill_(0.0)
+            step(ev)
+        torch.cuda.synchronize()
+        cold_ms = np.array([e0.elapsed_time(e1) for e0, e1 in cevs])
+        del scratch
     gbs = work.bytes / (ms_per_step * 1e-3) / 1e9
     tflops = work.flops / (ms_per_step * 1e-3) / 1e12
     avg_call_s = float(stage_ms.mean()) * 1e-3
@@ -272,6 +288,7 @@ def main():
                    "stage_kernels": STAGE_KERNELS[name],
                    "stage_us_mean": round(float(stage_ms.mean()) * 1e3, 2),
                    "stage_us_min": round(float(stage_ms.min()) * 1e3, 2),
+                   "stage_us_cold_mean": round(float(cold_ms.mean()) * 1e3, 2) if cold_ms.size else None,
                    "tflops": round(tflops, 3), "gbs": round(gbs, 2)},
         "roofline": roof,
     }
