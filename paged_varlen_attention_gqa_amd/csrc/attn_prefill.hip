@@ -216,7 +216,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   }
 
   // ---- K/V copy geometry ----
-  // wave w copies keys 4w..4w+3 of the tile (inside one page segment) with
+  // wave w copies keys 4w..4w+3 of each sub-tile (inside one page segment) with
   // one instruction for K and one for V; lane l copies one 16-byte chunk of
   // key 4w + l/16. K key 16h' + 4i + kk goes to LDS row 8i + 4h' + kk, so
   // that output register a of lane (h, n) of the QK MFMA is key 16h + a.
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
 #pragma unroll
   for (int u = 0; u < 2; ++u) bias_rd[u] = (uint32_t)(1024 * (n >> 4) + 16 * ((n & 15) + 16 * (3 - 2 * u - h)));
   const bool edge_row = E > 0 && row_ok && (my_row_abs == 0 || my_row_abs == (int64_t)P.T * P.H - 1);
-  // distances covered by a tile over the workgroup's rows: [p_lo - j0 - 31, p_hi - j0]
+  // distances covered by a sub-tile over the workgroup's rows: [p_lo - j0 - 31, p_hi - j0]
   const int p_lo = ia + L - S, p_hi = ib + L - S;
   // sub-tile at j0 -> 0: no key gets a bias, 1: every score does, 2: some do
   auto band_class = [&](int j0) -> int {
