@@ -518,8 +518,11 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
     issue_kv(kv_slot(0), 1, j0_of(tb) + kSub, page_of(j0_of(tb) + kSub));
     issue_bias_tile(1, j0_of(tb + 1));
     int page_next0 = page_of(j0_of(tb + 1)), page_next1 = page_of(j0_of(tb + 1) + kSub);
-    int kv_i = 0, b_i = 0;  // slots of tile s
-    for (int s = tb; s < te; ++s) {
+    // one stage; the slots of tile s (K/V: KVI, bias: BI) are constants of
+    // the instance, so that LDS addresses take immediate offsets
+    auto stage = [&](int s, auto kvi_c, auto bi_c) {
+      constexpr int kv_i = decltype(kvi_c)::value;
+      constexpr int b_i = decltype(bi_c)::value;
       wait_vm<4>();
       lds_barrier();
       // the page ids are used only from here on, so that the wait for
@@ -530,7 +533,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
       const int jn = j0_of(s + 1);
       issue_kv(kv_slot(kv_i ^ 1), 0, jn, page0);
       issue_kv(kv_slot(kv_i ^ 1), 1, jn + kSub, page1);
-      const int b_n = b_i == 0 ? 2 : b_i - 1;  // slot of tile s - 1 = slot of tile s + 2
+      constexpr int b_n = b_i == 0 ? 2 : b_i - 1;  // slot of tile s - 1 = slot of tile s + 2
       issue_bias_tile(b_n, j0_of(s + 2));
       page_next0 = page_of(j0_of(s + 2));
       page_next1 = page_of(j0_of(s + 2) + kSub);
@@ -578,9 +581,26 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
         }
         pv(kv, j, pb);
       }
-      kv_i ^= 1;
-      b_i = b_i == 2 ? 0 : b_i + 1;
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    // six stages cover every (K/V slot, bias slot) pair once
+    int s = tb;
+    for (; s + 6 <= te; s += 6) {
+      stage(s, I0{}, I0{});
+      stage(s + 1, I1{}, I1{});
+      stage(s + 2, I0{}, I2{});
+      stage(s + 3, I1{}, I0{});
+      stage(s + 4, I0{}, I1{});
+      stage(s + 5, I1{}, I2{});
     }
+    const int rem = te - s;
+    if (rem > 0) stage(s, I0{}, I0{});
+    if (rem > 1) stage(s + 1, I1{}, I1{});
+    if (rem > 2) stage(s + 2, I0{}, I2{});
+    if (rem > 3) stage(s + 3, I1{}, I0{});
+    if (rem > 4) stage(s + 4, I0{}, I1{});
     // the last copies re-read tiles nobody uses: let them land before the
     // LDS is released
     __builtin_amdgcn_s_waitcnt(0);
