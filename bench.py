@@ -148,17 +148,24 @@ def _cpu_baseline(case, name: str, budget_s: float) -> dict:
     done, t_total = [], 0.0
     elem = case.q.element_size()
     bound = BOUND[name]
-    for b in order:
-        toks = list(range(cu[b], cu[b + 1]))
-        if bound == "mfma":  # a bounded token sample of this request
-            toks = toks[-8:]
-        if not toks:
-            continue
-        t0 = time.perf_counter()
-        oracle.oracle_attention(**case.kwargs(), tokens=toks)
-        t_total += time.perf_counter() - t0
-        done.append((b, len(toks)))
-        if t_total > budget_s:
+    # passes over the requests until about 10 s of CPU time (a workload the
+    # oracle finishes sooner is repeated, for a steadier figure), at most budget_s
+    passes = 0
+    while t_total < min(10.0, budget_s):
+        passes += 1
+        for b in order:
+            toks = list(range(cu[b], cu[b + 1]))
+            if bound == "mfma":  # a bounded token sample of this request
+                toks = toks[-8:]
+            if not toks:
+                continue
+            t0 = time.perf_counter()
+            oracle.oracle_attention(**case.kwargs(), tokens=toks)
+            t_total += time.perf_counter() - t0
+            done.append((b, len(toks)))
+            if t_total > budget_s:
+                break
+        if t_total > budget_s or not done:
             break
     w = count_work(query_lens=[n for _, n in done], kv_lens=[klens[b] for b, _ in done],
                    num_heads=case.num_heads, num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
@@ -170,11 +177,12 @@ def _cpu_baseline(case, name: str, budget_s: float) -> dict:
     else:
         value, unit = w.bytes / t_total / 1e9, "GB/s"
     ntok = sum(n for _, n in done)
+    nreq = len(set(b for b, _ in done))
     return {"value": round(value, 6), "unit": unit, "cores": cores, "kind": "oracle",
-            "sample": f"{len(done)} of {B} requests ({ntok} query tokens, the last 8 of each request "
-                      f"for prefill), fp64 NumPy oracle, {t_total:.1f} s" if bound == "mfma" else
-                      f"{len(done)} of {B} requests ({ntok} query tokens), fp64 NumPy oracle, "
-                      f"{t_total:.1f} s"}
+            "sample": f"{nreq} of {B} requests ({ntok} query tokens over {passes} pass(es), the last 8 of "
+                      f"each request for prefill), fp64 NumPy oracle, {t_total:.1f} s" if bound == "mfma" else
+                      f"{nreq} of {B} requests ({ntok} query tokens over {passes} pass(es)), fp64 NumPy "
+                      f"oracle, {t_total:.1f} s"}
 
 
 def main():
