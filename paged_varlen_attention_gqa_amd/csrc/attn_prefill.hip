@@ -386,15 +386,21 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   const bool edge_wave = __builtin_amdgcn_ballot_w64(edge_row) != 0;
 
   // S^T = K Q^T for the tile in kv: register a of lane (h, n) is key j0 + 16h + a
-  auto qk = [&](const char* kv, f32x16_t& s) {
+  // both sub-tiles of the tile in kv, their MFMA chains interleaved (a
+  // chain's next step waits for its previous one)
+  auto qk2 = [&](const char* kv, f32x16_t* s) {
 #pragma unroll
-    for (int a = 0; a < 16; ++a) s[a] = 0.f;
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int kk = 0; kk < kD / 16; ++kk) {
-      const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kv + k_rd[kk]);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, kf),
-                                                  __builtin_bit_cast(bf16x8v_t, qreg[kk]), s, 0, 0, 0);
-    }
+      for (int a = 0; a < 16; ++a) s[j][a] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < kD / 16; ++kk)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kv + kSubBytes * j + k_rd[kk]);
+        s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, kf),
+                                                       __builtin_bit_cast(bf16x8v_t, qreg[kk]), s[j], 0, 0, 0);
+      }
   };
   // + bias / scale, by two more MFMAs when the band reaches the tile. The
   // masks sit in branches whose empty asm statements keep their computation
@@ -541,11 +547,9 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
       if (j0 + kKeys > L) zero_v_tail(kv, j0);
       // S^T = K Q^T (+ bias / scale) of the two sub-tiles
       f32x16_t sc[2];
+      qk2(kv, sc);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        qk(kv + kSubBytes * j, sc[j]);
-        add_bias(b_slot(b_i) + kBiasSub * j, j0 + kSub * j, sc[j]);
-      }
+      for (int j = 0; j < 2; ++j) add_bias(b_slot(b_i) + kBiasSub * j, j0 + kSub * j, sc[j]);
       mask_scores(j0, sc);
       // row max of the unscaled scores, scaled (log2 units); a new reference
       // only when it grows by more than the slack
