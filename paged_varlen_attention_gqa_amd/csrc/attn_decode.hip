@@ -587,7 +587,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_wg_split_kernel(AttnParam
 // workgroups; the piece of the k-th of them goes to split slot k. M is the
 // largest launched count for which no request has more than num_splits
 // pieces. Slots a request does not use get lse = -inf.
-template <int NW, int RING>
+template <int NW, int RING, int HALVES>
 __global__ __launch_bounds__(NW * 64) void attn_decode_balanced_kernel(AttnParams P,
                                                                        const int32_t* __restrict__ block_table) {
   __shared__ __attribute__((aligned(1024))) char ring0[NW * kSlotBytes];
@@ -598,9 +598,13 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_balanced_kernel(AttnParam
   const int lane = threadIdx.x & 63;
   __shared__ int prog[NW];
   prog[wave] = 0;
-  const int m = blockIdx.x;
-  const int M = gridDim.x;
-  const int g = blockIdx.y * NW + wave;  // KV head of this wave
+  // HALVES = 2: the workgroup serves NW / 2 heads with two waves each; wave
+  // w takes the second half of the workgroup's share when w >= NW / 2 (a
+  // workgroup then counts as two of the M workgroups that share the tiles)
+  constexpr int kHeads = NW / HALVES;
+  const int m = blockIdx.x * HALVES + wave / kHeads;
+  const int M = gridDim.x * HALVES;
+  const int g = blockIdx.y * kHeads + wave % kHeads;  // KV head of this wave
   if (g >= P.Hkv) return;
   const int K = P.splits;
 
@@ -699,7 +703,7 @@ namespace {
 
 // workgroups of the balanced kernel (NW waves) resident at once on the
 // device (all its compute units), queried once per device
-template <int NW>
+template <int NW, int HALVES>
 int balanced_slots() {
   static std::atomic<int> cached[64];
   int dev = 0;
@@ -709,7 +713,7 @@ int balanced_slots() {
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(attn_decode_balanced_kernel<NW, kDecodeRing>), NW * 64, 0) !=
+          &per_cu, reinterpret_cast<const void*>(attn_decode_balanced_kernel<NW, kDecodeRing, HALVES>), NW * 64, 0) !=
       hipSuccess)
     return 0;
   v = cus * per_cu;
@@ -717,15 +721,17 @@ int balanced_slots() {
   return v;
 }
 
-// one round of balanced workgroups of NW waves over the whole device
-template <int NW>
+// one round of balanced workgroups of NW waves (NW / HALVES heads each)
+// over the whole device
+template <int NW, int HALVES>
 int launch_balanced(const AttnParams& P, hipStream_t stream) {
-  const int slots = balanced_slots<NW>();
+  const int slots = balanced_slots<NW, HALVES>();
   if (slots <= 0) return -1;
-  const int groups = (P.Hkv + NW - 1) / NW;
+  constexpr int kHeads = NW / HALVES;
+  const int groups = (P.Hkv + kHeads - 1) / kHeads;
   const int per_group = slots / groups > 0 ? slots / groups : 1;
-  hipLaunchKernelGGL((attn_decode_balanced_kernel<NW, kDecodeRing>), dim3(per_group, groups), dim3(NW * 64), 0,
-                     stream, P, P.block_table);
+  hipLaunchKernelGGL((attn_decode_balanced_kernel<NW, kDecodeRing, HALVES>), dim3(per_group, groups),
+                     dim3(NW * 64), 0, stream, P, P.block_table);
   return 0;
 }
 
@@ -736,8 +742,11 @@ int launch_decode(const AttnParams& P, int head_dim, hipStream_t stream) {
   if (P.B == 0) return 0;
   const int groups = (P.Hkv + kDecodeWaves - 1) / kDecodeWaves;
   if (P.splits > 1 && P.B <= 64) {
-    const int rc = P.Hkv % kBalancedWaves == 0 ? launch_balanced<kBalancedWaves>(P, stream)
-                                               : launch_balanced<kDecodeWaves>(P, stream);
+    // 8 waves: 8 heads, or 4 heads with two waves each; other head counts
+    // take two 4-wave workgroups per compute unit
+    const int rc = P.Hkv % 8 == 0   ? launch_balanced<kBalancedWaves, 1>(P, stream)
+                   : P.Hkv % 4 == 0 ? launch_balanced<kBalancedWaves, 2>(P, stream)
+                                    : launch_balanced<kDecodeWaves, 1>(P, stream);
     if (rc != 0) return -1;
   } else if (P.splits == 1 && (int64_t)P.B * P.Hkv < kWgSplitMaxPairs && P.dec_chunk >= kWgSplitMinKeys) {
     // few (request, KV head) pairs with long key ranges and no workspace:
