@@ -129,6 +129,13 @@ __device__ __forceinline__ float dot2_bf16_ones(uint32_t w, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w), one, c, false);
 }
 
+// the middle value of x, 0 and hi (x clamped into [0, hi] for hi >= 0)
+__device__ __forceinline__ uint32_t clamp0(int x, int hi) {
+  uint32_t r;
+  asm("v_med3_i32 %0, %1, 0, %2" : "=v"(r) : "v"(x), "s"(__builtin_amdgcn_readfirstlane(hi)));
+  return r;
+}
+
 __device__ __forceinline__ float lane_swap32_max(float v) {
   const uint32_t u = __float_as_uint(v);
   auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
@@ -258,22 +265,31 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
 
   const int bs_log2 = P.bs_log2;
   const int bs_mask = P.bs - 1;
+  const int64_t head_bytes = (int64_t)g * kD * 2;
   const int32_t* __restrict__ bt_row = block_table + (int64_t)b * P.max_blocks;
-  const int last_page = ((L > 0 ? L : 1) - 1) >> bs_log2;
+  const uint32_t last_page = (uint32_t)((L > 0 ? L : 1) - 1) >> bs_log2;
   // raw page-table entry of this wave's keys of the sub-tile at j0 (a
   // scalar load; keys past L map to the request's last page)
   auto page_of = [&](int j0) -> int {
-    int pidx = (j0 + 4 * wave) >> bs_log2;
+    uint32_t pidx = (uint32_t)(j0 + 4 * wave) >> bs_log2;
     pidx = pidx > last_page ? last_page : pidx;
     return bt_row[pidx];
   };
   // caches under 4 GB: one resource each, a copy passes its page's offset
-  // as the scalar offset
+  // as the scalar offset (page ids are clamped into the pool first: the
+  // scalar offset is outside the resource's range check)
   const u32x4_t k_rsrc = make_rsrc(P.k, 0xffffffffu);
   const u32x4_t v_rsrc = make_rsrc(P.v, 0xffffffffu);
+  const uint32_t page_bytes = (uint32_t)P.bs * row_bytes;
+  // byte offset inside a page of this wave's first key of sub-tile j of a
+  // tile whose first key is a multiple of 64 (plus the tile's own offset
+  // inside the page when pages hold more than 64 keys)
+  uint32_t kv_in_page[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    kv_in_page[j] = (uint32_t)((kSub * j + 4 * wave) & bs_mask) * row_bytes + (uint32_t)head_bytes;
   const char* kbytes = reinterpret_cast<const char*>(P.k);
   const char* vbytes = reinterpret_cast<const char*>(P.v);
-  const int64_t head_bytes = (int64_t)g * kD * 2;
 
   // ---- relative-bias copy geometry ----
   // The wave's slice of a tile is, for each of its 32 rows, the 32 entries
@@ -305,15 +321,16 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   const int64_t my_row_abs = (int64_t)t * P.H + hq;
   const int rel_lane_elem = (int)(my_row_abs * E - reg_lo);  // row start, relative to the resource
   const int rel_last_piece = (int)(reg_hi - reg_lo) - 8;      // last piece start inside the resource
-  // the rows this lane copies (k = 0, 1): first entry of piece 0 of the
-  // tile at key 0, relative to the resource
-  int cp_elem[2];
+  const int rel_last_byte = 2 * rel_last_piece;
+  // the rows this lane copies (k = 0, 1): byte offset of the first entry of
+  // piece 0 of the tile at key 0, relative to the resource
+  int cp_byte[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int rc = min(r0 + 32 * wave + 16 * k + (lane & 15), nrows - 1);
     const int itok_c = rc / G;
     const int64_t row_abs_c = (int64_t)(t0 + itok_c) * P.H + g * G + rc % G;
-    cp_elem[k] = (int)(row_abs_c * E - reg_lo) + (itok_c + L - S) - 31 + 8 * (lane >> 4);
+    cp_byte[k] = 2 * ((int)(row_abs_c * E - reg_lo) + (itok_c + L - S) - 31 + 8 * (lane >> 4));
   }
   // where lane (h, n) finds its piece u of its row
   uint32_t bias_rd[2];
@@ -348,31 +365,30 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
     }
   }
 
-  // K/V copies of sub-tile j of the tile in kv, keys from j0 (its first key)
+  // K/V copies of sub-tile j of the tile in kv whose first key is j0 (a
+  // multiple of 64)
   auto issue_kv = [&](char* kv, int j, int j0, int page) {
     page = page < 0 ? 0 : (page >= P.num_blocks ? P.num_blocks - 1 : page);
     page = __builtin_amdgcn_readfirstlane(page);
-    const int key0 = j0 + 4 * wave;
     if constexpr (kWide) {
+      const int key0 = j0 + kSub * j + 4 * wave;
       const int64_t base = (((int64_t)page << bs_log2) + (key0 & bs_mask)) * row_bytes + head_bytes;
       dma16(make_rsrc(kbytes + base, 0x7fffffffu), kv + kSubBytes * j + k_dst, k_src);
       dma16(make_rsrc(vbytes + base, 0x7fffffffu), kv + kSubBytes * j + v_dst, v_src);
     } else {
-      const uint32_t off = (((uint32_t)page << bs_log2) + (uint32_t)(key0 & bs_mask)) * row_bytes + (uint32_t)head_bytes;
+      const uint32_t off = __builtin_amdgcn_readfirstlane((uint32_t)page * page_bytes + kv_in_page[j] +
+                                                          (uint32_t)(j0 & bs_mask) * row_bytes);
       dma16_soff(k_rsrc, kv + kSubBytes * j + k_dst, k_src, off);
       dma16_soff(v_rsrc, kv + kSubBytes * j + v_dst, v_src, off);
     }
   };
-  // bias copies of the sub-tile at j0 into bias (the wave's slice)
-  auto issue_bias = [&](char* my_bias, int j0) {
-    // a tile that no bias reaches re-reads the row's first entries (cached),
-    // so that it costs no HBM traffic
-    const bool no_bias = band_class(j0) == 0;
+  // bias copies of the sub-tile at j0 into bias (the wave's slice); a
+  // sub-tile that no bias reaches (no_bias) re-reads the first entries of
+  // the resource (cached), so that it costs no HBM traffic
+  auto issue_bias = [&](char* my_bias, int j0, bool no_bias) {
+    const int hi = no_bias ? 0 : rel_last_byte;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int at = no_bias ? 0 : min(max(cp_elem[k] - j0, 0), rel_last_piece);
-      dma16(rel_rsrc, my_bias + 1024 * k, (uint32_t)at * 2u);
-    }
+    for (int k = 0; k < 2; ++k) dma16(rel_rsrc, my_bias + 1024 * k, clamp0(cp_byte[k] - 2 * j0, hi));
   };
 
   f32x16_t oacc[kD / 32];  // O^T: dim tile mt, lane (h, n) reg a = dim 32mt + 8(a/4) + 4h + a%4
@@ -401,43 +417,53 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
         s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, kf),
                                                        __builtin_bit_cast(bf16x8v_t, qreg[kk]), s[j], 0, 0, 0);
       }
+    // K operand reads run three steps ahead of the matrix instructions
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
   };
-  // + bias / scale, by two more MFMAs when the band reaches the tile. The
-  // masks sit in branches whose empty asm statements keep their computation
-  // inside (no selects computed on every tile): band masks only where the
-  // band covers part of the tile, the shift only in waves holding the first
-  // or last row of rel_logits.
-  auto add_bias = [&](const char* my_bias, int j0, f32x16_t& s) {
+  // + bias / scale, by two more MFMAs when the band reaches the tile. Two
+  // rare cases first rewrite the wave's slice in LDS (in branches that leave
+  // no values behind, so that the common path reads the slice as it is):
+  // where the band covers part of the tile, entries outside it are zeroed;
+  // in waves holding the first or last row of rel_logits, pieces read at a
+  // clamped position are shifted back into place.
+  auto add_bias = [&](char* my_bias, int j0, f32x16_t& s) {
     const int bc = band_class(j0);
     if (bc == 0) return;
-    // piece u: entry x is distance e_lo0 - 16u + x (key 16u + 8h + 7 - x)
-    u32x4_t bb[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) bb[u] = *reinterpret_cast<const u32x4_t*>(my_bias + bias_rd[u]);
-    const int e_lo0 = p - (j0 + 8 * h) - 7;
-    if (edge_wave) {
+    if (bc == 2 || edge_wave) {
       asm volatile("");
-      // first and last row of the tensor: a piece read at `at` instead of
-      // `want` has its entries moved back by want - at
+      // piece u: entry x is distance e_lo0 - 16u + x (key 16u + 8h + 7 - x)
+      const int e_lo0 = p - (j0 + 8 * h) - 7;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int want = rel_lane_elem + e_lo0 - 16 * u;
-        const int at = min(max(want, 0), rel_last_piece);
-        bb[u] = shift_entries(bb[u], want - at);
-      }
-    }
-    if (bc == 2) {
-      asm volatile("");
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
+        u32x4_t v = *reinterpret_cast<const u32x4_t*>(my_bias + bias_rd[u]);
+        if (edge_wave) {
+          // a piece read at `at` instead of `want` has its entries moved
+          // back by want - at
+          const int want = rel_lane_elem + e_lo0 - 16 * u;
+          const int at = min(max(want, 0), rel_last_piece);
+          v = shift_entries(v, want - at);
+        }
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const int e = e_lo0 - 16 * u + 2 * w;
           const uint32_t lo_ok = (uint32_t)e < (uint32_t)E ? 0xffffu : 0u;
           const uint32_t hi_ok = (uint32_t)(e + 1) < (uint32_t)E ? 0xffff0000u : 0u;
-          bb[u][w] &= lo_ok | hi_ok;
+          v[w] &= lo_ok | hi_ok;
         }
+        *reinterpret_cast<u32x4_t*>(my_bias + bias_rd[u]) = v;
+      }
+      // the common path below reloads the slice
+      asm volatile("" ::: "memory");
     }
+    u32x4_t bb[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) bb[u] = *reinterpret_cast<const u32x4_t*>(my_bias + bias_rd[u]);
 #pragma unroll
     for (int u = 0; u < 2; ++u)
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, bias_sel[u]),
@@ -515,13 +541,13 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
     auto kv_slot = [&](int i) { return kv_buf + i * kKV; };
     auto b_slot = [&](int i) { return bias_buf + i * (kWaves * kBiasWave) + wave * kBiasWave; };
     auto issue_bias_tile = [&](int slot, int j0) {
-      issue_bias(b_slot(slot), j0);
-      issue_bias(b_slot(slot) + kBiasSub, j0 + kSub);
+      issue_bias(b_slot(slot), j0, band_class(j0) == 0);
+      issue_bias(b_slot(slot) + kBiasSub, j0 + kSub, band_class(j0 + kSub) == 0);
     };
     // copies of the stages before tb: bias tb, K/V tb, bias tb + 1
     issue_bias_tile(0, j0_of(tb));
     issue_kv(kv_slot(0), 0, j0_of(tb), page_of(j0_of(tb)));
-    issue_kv(kv_slot(0), 1, j0_of(tb) + kSub, page_of(j0_of(tb) + kSub));
+    issue_kv(kv_slot(0), 1, j0_of(tb), page_of(j0_of(tb) + kSub));
     issue_bias_tile(1, j0_of(tb + 1));
     int page_next0 = page_of(j0_of(tb + 1)), page_next1 = page_of(j0_of(tb + 1) + kSub);
     // one stage; the slots of tile s (K/V: KVI, bias: BI) are constants of
@@ -537,12 +563,13 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
       asm volatile("" : "+s"(page0), "+s"(page1));
       const int j0 = j0_of(s);
       const int jn = j0_of(s + 1);
+      const int j2 = j0_of(s + 2);
       issue_kv(kv_slot(kv_i ^ 1), 0, jn, page0);
-      issue_kv(kv_slot(kv_i ^ 1), 1, jn + kSub, page1);
+      issue_kv(kv_slot(kv_i ^ 1), 1, jn, page1);
       constexpr int b_n = b_i == 0 ? 2 : b_i - 1;  // slot of tile s - 1 = slot of tile s + 2
-      issue_bias_tile(b_n, j0_of(s + 2));
-      page_next0 = page_of(j0_of(s + 2));
-      page_next1 = page_of(j0_of(s + 2) + kSub);
+      issue_bias_tile(b_n, j2);
+      page_next0 = page_of(j2);
+      page_next1 = page_of(j2 + kSub);
       char* kv = kv_slot(kv_i);
       if (j0 + kKeys > L) zero_v_tail(kv, j0);
       // S^T = K Q^T (+ bias / scale) of the two sub-tiles
