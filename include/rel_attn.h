@@ -57,7 +57,7 @@ extern "C" {
  * chosen for 256 compute units:
  *   - decode-shaped calls (max_query_len * num_heads / num_kv_heads <= 16):
  *     the decode kernel shares the batch's keys evenly among one round of
- *     workgroups (4 KV heads each) and cuts a request into at most this many
+ *     workgroups (4 or 8 KV heads each) and cuts a request into at most this many
  *     pieces; the count leaves room for requests of unequal length, and
  *     pieces hold at least 256 keys (max_kv_len / 256 + 1 at most);
  *   - other calls: work units (requests x KV heads x 64-row query tiles)

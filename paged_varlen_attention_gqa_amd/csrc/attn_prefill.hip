@@ -302,7 +302,8 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   // on each side (inside the tensor). A piece is read from its position
   // clamped into the resource: with E >= 8 a piece moved that way holds an
   // entry in 0 <= d < E only in the first or last row of the tensor, whose
-  // lanes shift the entries back into place in registers.
+  // lanes shift the entries back into place (rewriting the slice in LDS
+  // before the bias is added).
   const int E = P.E;
   const int64_t tensor_elems = (int64_t)P.T * P.H * E;
   int64_t reg_lo = 0, reg_hi = 0;
