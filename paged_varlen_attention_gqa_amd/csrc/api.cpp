@@ -20,10 +20,11 @@ constexpr int kTargetWorkgroups = 1024;
 // Fewest keys worth giving one split.
 constexpr int kMinKeysPerSplit = 256;
 // Decode-shaped calls (one 16-column tile of query rows per KV head): the
-// balanced decode kernel runs one round of 512 workgroups (2 per compute unit
-// on 256 CUs), each over 4 KV heads; splits are the most pieces one request
-// may be cut into, with room for requests of unequal length, and a piece
-// should hold at least 256 keys.
+// balanced decode kernel cuts the batch's tiles into one round of 512 pieces
+// per 4 KV heads on 256 CUs (two 4-wave workgroups per compute unit, or one
+// 8-wave workgroup over 8 heads, or over 4 heads in two halves); splits are
+// the most pieces one request may be cut into, with room for requests of
+// unequal length, and a piece should hold at least 256 keys.
 constexpr int kDecodeWorkgroups = 512;
 constexpr int kDecodeHeadsPerWorkgroup = 4;
 constexpr int kDecodeMinKeysPerPiece = 256;
