@@ -132,6 +132,11 @@ EDGE = [
          num_kv_heads=4, head_dim=128, block_size=64, rel_extent=2048, window_size=(4095, 0)),
     dict(name="fp32_noncausal_g4", query_lens=[1, 7], kv_lens=[90, 7], num_heads=8, num_kv_heads=2,
          head_dim=64, block_size=8, rel_extent=5, causal=False, dtype=torch.float32),
+    # prefill with pages of more than 64 keys (a 64-key tile starts inside a page)
+    dict(name="prefill_block_128", query_lens=[70, 130], kv_lens=[300, 501], num_heads=16, num_kv_heads=2,
+         head_dim=128, block_size=128, rel_extent=200),
+    dict(name="prefill_block_256_window", query_lens=[50, 9], kv_lens=[700, 260], num_heads=8, num_kv_heads=1,
+         head_dim=128, block_size=256, rel_extent=64, window_size=(300, 0)),
 ]
 
 
