@@ -39,6 +39,7 @@ def test_graph_replay(name):
     spec = CASES[name]
     cases = [make_case(name=name, seed=s, **spec) for s in (5, 6, 7, 8)]
     kw = device_case(cases[0])
+    base = {k: kw[k].clone() for k in ("key_cache", "value_cache")}
     T, H, D = kw["q"].shape
     local = spec.get("window_size", (-1, -1)) != (-1, -1)
     ns = rel_attn_num_splits(is_local=local, batch_size=len(spec["query_lens"]),
@@ -57,9 +58,15 @@ def test_graph_replay(name):
     torch.cuda.synchronize()
     for i, c in enumerate(cases):
         src = device_case(c)
-        # new values in the captured buffers (the metadata stays the captured one)
-        for k in ("q", "key_cache", "value_cache", "rel_logits"):
+        # new values in the captured buffers; the metadata stays the captured
+        # one, so the caches keep the captured layout: new finite values in the
+        # slots the captured call references, NaN in the others
+        for k in ("q", "rel_logits"):
             kw[k].copy_(src[k])
+        for k in ("key_cache", "value_cache"):
+            used = torch.isfinite(base[k])
+            vals = torch.where(torch.isfinite(src[k]), src[k], torch.full_like(src[k], 0.25))
+            kw[k].copy_(torch.where(used, vals, torch.full_like(vals, float("nan"))))
         out.zero_()
         ref = rel_attn_fwd(**kw, num_splits=ns)  # eager, its own output and workspace
         torch.cuda.synchronize()
