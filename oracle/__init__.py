@@ -26,7 +26,10 @@ windows are inclusive ``[p - left, p + right]``; a query with no visible key
 outputs zeros.
 
 Every function here has at least one pin in ``tests/test_oracle_pins.py``; none
-is "parity unpinned".
+is "parity unpinned". The log-sum-exp that ``oracle_attention(..., return_lse=True)``
+returns is pinned by hand-derived values (``tests/golden/hand_cases.json``),
+``ln n`` for ``n`` equal scores, a single visible key's own score, and
+``torch.logsumexp`` over the masked fp64 score matrix.
 """
 
 from .attention import (  # noqa: F401

@@ -214,10 +214,9 @@ def oracle_bruteforce(q, key_cache, value_cache, *, block_table, cache_seqlens, 
     """Scalar loops over every (token, head, key); tiny inputs only.
 
     Written independently of :func:`oracle_attention`: each key is fetched
-    through its page, each mask condition is tested per key, and the bias is
-    looked up with the pages' clamp-then-compare rule (clamp ``d`` into
-    ``[0, rel_extent - 1]``, read that entry, keep it only if the clamp did not
-    move ``d``).
+    through its page, each mask condition is tested per key, and the bias of
+    key ``j`` is the entry at distance ``d = p - j`` of the query's
+    ``rel_logits`` row when ``0 <= d < rel_extent``, else 0.
     """
     del max_seqlen_q
     bt = _ints(block_table).tolist()
@@ -253,12 +252,10 @@ def oracle_bruteforce(q, key_cache, value_cache, *, block_table, cache_seqlens, 
                     dot = 0.0
                     for e in range(D):
                         dot += qv[t, h, e] * kc[page, slot, g, e]
-                    bias = 0.0
-                    if rel_extent > 0:
-                        d = p - j
-                        idx = d if d >= 0 else 0
-                        idx = idx if idx < rel_extent else rel_extent - 1
-                        bias = rl[t, h, idx] if d == idx else 0.0
+                    # the distance of key j behind the query; only
+                    # distances 0 .. rel_extent-1 have a bias entry
+                    d = p - j
+                    bias = rl[t, h, d] if 0 <= d < rel_extent else 0.0
                     scores.append(softmax_scale * dot + bias)
                     vrows.append(vc[page, slot, g, :])
                 if not scores:

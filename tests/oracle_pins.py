@@ -43,6 +43,14 @@ def load_golden():
     return out
 
 
+def load_golden_lse():
+    """(name, kwargs, expected_lse) of every golden case; "-inf" marks a row with no visible key."""
+    with open(GOLDEN) as f:
+        data = json.load(f)
+    lses = {c["name"]: np.array([[float(x) for x in row] for row in c["expected_lse"]]) for c in data["cases"]}
+    return [(name, kw, lses[name]) for name, kw, _ in load_golden()]
+
+
 def small_case(seed=0, **over):
     spec = dict(query_lens=[3, 1, 6], kv_lens=[9, 13, 6], num_heads=4, num_kv_heads=2, head_dim=8,
                 block_size=4, rel_extent=5, causal=True, window_size=(-1, -1),
@@ -287,9 +295,105 @@ def pin_bruteforce(oa, ob, osc):
                     assert np.allclose(a, b, rtol=0, atol=1e-12), (causal, win, E, H, Hkv, bs)
 
 
+def _same_lse(got, exp, atol):
+    """Equal within atol, with -inf exactly where the expected value is -inf."""
+    got = np.asarray(got, dtype=np.float64)
+    exp = np.asarray(exp, dtype=np.float64)
+    assert got.shape == exp.shape, (got.shape, exp.shape)
+    assert np.array_equal(np.isneginf(got), np.isneginf(exp)), (got, exp)
+    fin = np.isfinite(exp)
+    assert np.all(np.isfinite(got[fin])), got
+    assert np.allclose(got[fin], exp[fin], rtol=0, atol=atol), np.abs(got[fin] - exp[fin]).max()
+
+
+def pin_lse_golden(oa, ob, osc):
+    """Log-sum-exp of the hand-derived cases (ln 4, ln 5, ..., -inf for a row with no key)."""
+    for name, kw, exp in load_golden_lse():
+        _, lse = oa(**kw, return_lse=True)
+        _same_lse(lse, exp, 1e-12)
+
+
+def _mask_count(S, L, causal, window):
+    """Visible-key mask (S, L) built from torch.tril / torch.triu band offsets (query i at p = i + L - S)."""
+    o = L - S
+    m = torch.ones(S, L, dtype=torch.bool)
+    if causal:
+        m &= torch.tril(torch.ones(S, L, dtype=torch.bool), diagonal=o)
+    wl, wr = window
+    if wl >= 0:
+        m &= torch.triu(torch.ones(S, L, dtype=torch.bool), diagonal=o - wl)
+    if wr >= 0:
+        m &= torch.tril(torch.ones(S, L, dtype=torch.bool), diagonal=o + wr)
+    return m
+
+
+def pin_lse_uniform(oa, ob, osc):
+    """q = 0 and no bias make every visible score 0, so the log-sum-exp is ln(visible keys)."""
+    for causal, win in ((True, (-1, -1)), (True, (3, 0)), (False, (2, 1)), (False, (-1, -1))):
+        case = small_case(seed=20, rel_extent=0, causal=causal, window_size=win,
+                          query_lens=[3, 1, 6, 2], kv_lens=[9, 13, 6, 2])
+        case.cache_seqlens[3] = 1  # two queries over one key: the first sits at p = -1
+        case.q.zero_()
+        _, lse = oa(**case.kwargs(), return_lse=True)
+        cu = case.cu_seqlens_q.tolist()
+        for b, L in enumerate(case.cache_seqlens.tolist()):
+            S = cu[b + 1] - cu[b]
+            n = _mask_count(S, L, causal, win).sum(dim=1).numpy().astype(np.float64)
+            exp = np.where(n > 0, np.log(np.maximum(n, 1.0)), -np.inf)
+            for h in range(case.num_heads):
+                _same_lse(lse[cu[b]:cu[b + 1], h], exp, 1e-12)
+
+
+def pin_lse_single_key(oa, ob, osc):
+    """Window (0, 0): one visible key, so the log-sum-exp is that key's own score."""
+    case = small_case(seed=21, window_size=(0, 0))
+    _, lse = oa(**case.kwargs(), return_lse=True)
+    cu = case.cu_seqlens_q.tolist()
+    G = case.num_heads // case.num_kv_heads
+    for b, L in enumerate(case.cache_seqlens.tolist()):
+        S = cu[b + 1] - cu[b]
+        for i in range(S):
+            t, p = cu[b] + i, i + L - S
+            page = int(case.block_table[b, p // case.block_size])
+            for h in range(case.num_heads):
+                k = case.key_cache[page, p % case.block_size, h // G].double()
+                s = case.softmax_scale * float(torch.dot(case.q[t, h].double(), k)) + \
+                    float(case.rel_logits[t, h, 0])
+                assert abs(lse[t, h] - s) <= 1e-12, (t, h, lse[t, h], s)
+
+
+def pin_lse_logsumexp(oa, ob, osc):
+    """torch.logsumexp (a library reduction) over the fp64 masked score matrix built with torch ops."""
+    for causal, win in ((True, (-1, -1)), (False, (2, 3)), (True, (4, 0))):
+        case = small_case(seed=22, rel_extent=6, causal=causal, window_size=win, rel_std=3.0,
+                          query_lens=[3, 1, 6, 2], kv_lens=[9, 13, 6, 2])
+        case.cache_seqlens[3] = 1  # two queries over one key: the first sits at p = -1
+        _, lse = oa(**case.kwargs(), return_lse=True)
+        cu = case.cu_seqlens_q.tolist()
+        G = case.num_heads // case.num_kv_heads
+        E = case.rel_extent
+        for b, L in enumerate(case.cache_seqlens.tolist()):
+            S = cu[b + 1] - cu[b]
+            bs = case.block_size
+            pages = case.block_table[b, : (L + bs - 1) // bs].long()
+            K = case.key_cache[pages].reshape(-1, case.num_kv_heads, case.head_dim)[:L].double()
+            Q = case.q[cu[b]: cu[b + 1]].double()
+            dist = (torch.arange(S)[:, None] + (L - S)) - torch.arange(L)[None, :]
+            mask = _mask_count(S, L, causal, win)
+            for h in range(case.num_heads):
+                sc = case.softmax_scale * (Q[:, h, :] @ K[:, h // G, :].T)
+                R = case.rel_logits[cu[b]: cu[b + 1], h, :].double()
+                inr = (dist >= 0) & (dist < E)
+                bias = torch.gather(R, 1, dist.clamp(0, E - 1)) * inr
+                sc = torch.where(mask, sc + bias, torch.tensor(float("-inf"), dtype=torch.float64))
+                exp = torch.logsumexp(sc, dim=1).numpy()
+                _same_lse(lse[cu[b]:cu[b + 1], h], exp, 1e-12)
+
+
 ALL_PINS = [pin_golden, pin_sdpa_no_bias, pin_top_left_causal, pin_one_hot_bias,
             pin_single_visible_key, pin_gqa_expansion, pin_page_permutation, pin_constant_bias,
-            pin_extent_endpoint, pin_split_combine, pin_request_order, pin_bruteforce]
+            pin_extent_endpoint, pin_split_combine, pin_request_order, pin_lse_golden,
+            pin_lse_uniform, pin_lse_single_key, pin_lse_logsumexp, pin_bruteforce]
 
 # Pins that do not compare two forms of the oracle with each other
 INDEPENDENT_PINS = [p for p in ALL_PINS if p is not pin_bruteforce]

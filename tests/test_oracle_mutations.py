@@ -27,7 +27,10 @@ MUTATIONS = [
     ("distance_sign", "d = p[:, None] - j[None, :]", "d = j[None, :] - p[:, None]"),
     ("distance_sign_bf", "d = p - j", "d = j - p"),
     ("extent_inclusive", "(d >= 0) & (d < rel_extent)", "(d >= 0) & (d <= rel_extent)"),
-    ("extent_no_compare_bf", "bias = rl[t, h, idx] if d == idx else 0.0", "bias = rl[t, h, idx]"),
+    ("extent_no_lower_bound_bf", "bias = rl[t, h, d] if 0 <= d < rel_extent else 0.0",
+     "bias = rl[t, h, d] if d < rel_extent else 0.0"),
+    ("extent_inclusive_bf", "bias = rl[t, h, d] if 0 <= d < rel_extent else 0.0",
+     "bias = rl[t, h, min(d, rel_extent - 1)] if 0 <= d <= rel_extent else 0.0"),
     ("scale_dropped", "s = softmax_scale * (qh @ K.T)", "s = (qh @ K.T)"),
     ("scale_dropped_bf", "scores.append(softmax_scale * dot + bias)", "scores.append(dot + bias)"),
     ("bias_scaled", "s = s + np.where(in_range, bias, 0.0)",
@@ -49,6 +52,13 @@ MUTATIONS = [
     ("combine_unweighted", "out[t0 + r, h, :] = sum(math.exp(lk - LSE) * pk for lk, pk in zip(lses, parts))",
      "out[t0 + r, h, :] = sum(pk for lk, pk in zip(lses, parts)) / len(parts)"),
     ("combine_lse_no_log", "lses.append(m_k + math.log(l_k))", "lses.append(m_k + l_k)"),
+    # the row log-sum-exp returned with return_lse=True
+    ("lse_max_plus_sum", "m + np.log(np.where(has, l, 1.0))", "m + np.where(has, l, 1.0)"),
+    ("lse_log2", "m + np.log(np.where(has, l, 1.0))", "m + np.log2(np.where(has, l, 1.0))"),
+    ("lse_max_dropped", "m + np.log(np.where(has, l, 1.0))", "np.log(np.where(has, l, 1.0))"),
+    ("lse_empty_zero", "np.where(has, m + np.log(np.where(has, l, 1.0)), NEG_INF)",
+     "np.where(has, m + np.log(np.where(has, l, 1.0)), 0.0)"),
+    ("lse_sum_without_max", "l = w.sum(axis=1)", "l = w.sum(axis=1) * np.exp(m)"),
 ]
 
 
