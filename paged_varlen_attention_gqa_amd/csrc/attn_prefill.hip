@@ -13,11 +13,15 @@
 //     m = 8i + 4h + k holds key 16h + 4i + k, so that output register a of
 //     lane (h, n) of v_mfma_f32_32x32x16_bf16 is key 16h + a;
 //   * the relative bias is added by the matrix cores too: two more MFMAs per
-//     sub-tile multiply a constant 0 / (1/scale) selection matrix by the
-//     bias as the B operand, whose 8 k slots per lane are 8 consecutive
-//     entries of one rel_logits row (16-byte pieces of 64-byte runs per row,
-//     copied into aligned LDS slots), so the bias costs no vector-ALU work
-//     per score;
+//     sub-tile multiply a constant one-hot selection matrix by the bias as
+//     the B operand, whose 8 k slots per lane are 8 consecutive entries of
+//     one rel_logits row (16-byte pieces of 64-byte runs per row, copied into
+//     aligned LDS slots). They start the sub-tile's score accumulator, and
+//     the QK^T MFMAs accumulate on top. The selection value is
+//     1/softmax_scale when that is a bf16 number; otherwise it is 1 and the
+//     accumulator is multiplied by 1/softmax_scale in fp32 before the QK^T
+//     MFMAs. Either way the softmax sees softmax_scale * (q.k + bias /
+//     softmax_scale) with the bias exact to fp32 rounding;
 //   * V^T operands come from the row-major V tile through the LDS transpose
 //     read (lane (g, i) of a 16-lane group receives V[4g + k][col0 + i]);
 //     O^T += V^T P^T takes the probabilities, packed to bf16, as its B
@@ -152,9 +156,12 @@ __device__ __forceinline__ float lane_swap32_sum(float v) {
 // it also wait for the copies in flight)
 // kWide: a cache spans 4 GB or more, so that K/V copies build a resource
 // per page instead of passing a 32-bit offset
-template <bool kWide>
+// kExactSel: 1/softmax_scale (inv_scale) is a bf16 number and selects the
+// bias directly
+template <bool kWide, bool kExactSel>
 __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
-                                                                 const int32_t* __restrict__ block_table) {
+                                                                 const int32_t* __restrict__ block_table,
+                                                                 float inv_scale) {
   // the K/V ring, then the bias ring (160 KB)
   __shared__ __attribute__((aligned(1024))) char lds[kKvSlots * kKV + kBiasSlots * kWaves * kBiasWave];
   char* const kv_buf = lds;
@@ -348,13 +355,13 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   };
   // A operand of the bias MFMAs: lane (h', m) holds row m (key sigma(m)) and
   // k slots 8h' + x; slot x of part u stands for key 16u + 8h' + 7 - x; the
-  // entry is 1/scale where that key is sigma(m), else 0.
+  // entry is the selection value (1/scale or 1) where that key is sigma(m),
+  // else 0.
   u32x4_t bias_sel[2];
   {
     const int m = n;
     const int sig = 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
-    const float inv_scale = (P.scale_log2 != 0.f) ? kLog2e / P.scale_log2 : 0.f;
-    const uint32_t cbits = pack_bf16x2(inv_scale, 0.f) & 0xffffu;
+    const uint32_t cbits = kExactSel ? (pack_bf16x2(inv_scale, 0.f) & 0xffffu) : 0x3f80u;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int x = 16 * u + 8 * h + 7 - sig;  // slot that matches, if in 0..7
@@ -402,14 +409,10 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   const float scale_log2 = P.scale_log2;  // scores are acc * scale_log2 (bias included)
   const bool edge_wave = __builtin_amdgcn_ballot_w64(edge_row) != 0;
 
-  // S^T = K Q^T for the tile in kv: register a of lane (h, n) is key j0 + 16h + a
-  // both sub-tiles of the tile in kv, their MFMA chains interleaved (a
-  // chain's next step waits for its previous one)
+  // S^T += K Q^T for both sub-tiles of the tile in kv: register a of lane
+  // (h, n) is key j0 + 16h + a; the two MFMA chains interleaved (a chain's
+  // next step waits for its previous one)
   auto qk2 = [&](const char* kv, f32x16_t* s) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int a = 0; a < 16; ++a) s[j][a] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < kD / 16; ++kk)
 #pragma unroll
@@ -427,13 +430,17 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
   };
-  // + bias / scale, by two more MFMAs when the band reaches the tile. Two
-  // rare cases first rewrite the wave's slice in LDS (in branches that leave
-  // no values behind, so that the common path reads the slice as it is):
-  // where the band covers part of the tile, entries outside it are zeroed;
-  // in waves holding the first or last row of rel_logits, pieces read at a
-  // clamped position are shifted back into place.
-  auto add_bias = [&](char* my_bias, int j0, f32x16_t& s) {
+  // The start of the score accumulator of the sub-tile at j0: bias / scale,
+  // by two MFMAs (and, when the selection value is 1, an fp32 multiply)
+  // when the band reaches the sub-tile, else 0. Two rare cases first rewrite
+  // the wave's slice in LDS (in branches that leave no values behind, so
+  // that the common path reads the slice as it is): where the band covers
+  // part of the tile, entries outside it are zeroed; in waves holding the
+  // first or last row of rel_logits, pieces read at a clamped position are
+  // shifted back into place.
+  auto bias_acc = [&](char* my_bias, int j0, f32x16_t& s) {
+#pragma unroll
+    for (int a = 0; a < 16; ++a) s[a] = 0.f;
     const int bc = band_class(j0);
     if (bc == 0) return;
     if (bc == 2 || edge_wave) {
@@ -469,6 +476,10 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
     for (int u = 0; u < 2; ++u)
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, bias_sel[u]),
                                                   __builtin_bit_cast(bf16x8v_t, bb[u]), s, 0, 0, 0);
+    if constexpr (!kExactSel) {
+#pragma unroll
+      for (int a = 0; a < 16; ++a) s[a] *= inv_scale;
+    }
   };
   // scores of keys a row does not see -> -inf (only on tiles some row does
   // not see whole)
@@ -573,11 +584,11 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
       page_next1 = page_of(j2 + kSub);
       char* kv = kv_slot(kv_i);
       if (j0 + kKeys > L) zero_v_tail(kv, j0);
-      // S^T = K Q^T (+ bias / scale) of the two sub-tiles
+      // S^T = bias / scale + K Q^T of the two sub-tiles
       f32x16_t sc[2];
-      qk2(kv, sc);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) add_bias(b_slot(b_i) + kBiasSub * j, j0 + kSub * j, sc[j]);
+      for (int j = 0; j < 2; ++j) bias_acc(b_slot(b_i) + kBiasSub * j, j0 + kSub * j, sc[j]);
+      qk2(kv, sc);
       mask_scores(j0, sc);
       // row max of the unscaled scores, scaled (log2 units); a new reference
       // only when it grows by more than the slack
@@ -670,13 +681,22 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
 
 }  // namespace
 
+// whether 1/softmax_scale (fp32) is a bf16 number (low 16 bits zero)
+static bool inv_scale_is_bf16(float inv) {
+  uint32_t u;
+  __builtin_memcpy(&u, &inv, 4);
+  return (u & 0xffffu) == 0u;
+}
+
 bool prefill_supported(const AttnParams& P, int dtype_bf16, int head_dim) {
   // resource offsets are 32-bit: the bias rows of one wave must span less
   // than 2 GB (E * H * (32/G + 2) entries)
   const int64_t span = (int64_t)P.E * P.H * (32 / P.G + 2) * 2 + 256;
-  // the scores stay unscaled until the exponent: the scale must be positive
+  // the scores stay unscaled until the exponent: the scale must be positive,
+  // with a finite reciprocal
+  const float inv = P.scale_log2 > 0.f ? kLog2e / P.scale_log2 : 0.f;
   return dtype_bf16 && head_dim == kD && P.bs_log2 >= 4 && span < 0x7fffffff && P.scale_log2 > 0.f &&
-         (P.E == 0 || P.E >= 8);
+         inv > 0.f && inv < 3.0e38f && (P.E == 0 || P.E >= 8);
 }
 
 int launch_prefill(const AttnParams& P, hipStream_t stream) {
@@ -687,10 +707,19 @@ int launch_prefill(const AttnParams& P, hipStream_t stream) {
   // past its first key's row)
   const uint64_t row = (uint64_t)P.Hkv * kD * 2;
   const uint64_t cache_bytes = (uint64_t)P.num_blocks * ((uint64_t)1 << P.bs_log2) * row;
-  if (cache_bytes + 4 * row < ((uint64_t)1 << 32))
-    hipLaunchKernelGGL(attn_prefill_kernel<false>, grid, dim3(kWaves * 64), 0, stream, P, P.block_table);
+  const bool wide = cache_bytes + 4 * row >= ((uint64_t)1 << 32);
+  // 1/softmax_scale from the scale in log2 units (softmax_scale * log2 e)
+  const float inv_scale = kLog2e / P.scale_log2;
+  const bool exact = inv_scale_is_bf16(inv_scale);
+  const dim3 block(kWaves * 64);
+  if (!wide && exact)
+    hipLaunchKernelGGL((attn_prefill_kernel<false, true>), grid, block, 0, stream, P, P.block_table, inv_scale);
+  else if (!wide)
+    hipLaunchKernelGGL((attn_prefill_kernel<false, false>), grid, block, 0, stream, P, P.block_table, inv_scale);
+  else if (exact)
+    hipLaunchKernelGGL((attn_prefill_kernel<true, true>), grid, block, 0, stream, P, P.block_table, inv_scale);
   else
-    hipLaunchKernelGGL(attn_prefill_kernel<true>, grid, dim3(kWaves * 64), 0, stream, P, P.block_table);
+    hipLaunchKernelGGL((attn_prefill_kernel<true, false>), grid, block, 0, stream, P, P.block_table, inv_scale);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
