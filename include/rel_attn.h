@@ -198,6 +198,39 @@ int rel_attn_fwd_lse(const void* q, const void* key_cache, const void* value_cac
                      void* stream);
 
 /*
+ * rel_attn_fwd_noalloc - rel_attn_fwd for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. Same arguments as rel_attn_fwd without
+ * the three workspace ones; same checks, same return codes, same results.
+ *
+ * With num_splits > 1 the split partials go to a static device array of
+ * rel_attn_noalloc_scratch_bytes() bytes (32 MiB) that the library keeps on
+ * every GPU it runs on until the process ends, not to a caller workspace. A
+ * call whose workspace (rel_attn_workspace_bytes) exceeds that size returns
+ * REL_ATTN_EWORKSPACE and launches nothing. The call never allocates or frees
+ * device memory. Every argument check runs before any device is touched.
+ *
+ * All calls on one GPU share that GPU's array, which keeps the last call's
+ * contents (nothing in it needs to start at zero): calls that overlap on one
+ * GPU (on different streams, or graphs replayed at the same time) race and
+ * give wrong results, so serialise them. The stream must belong to the
+ * current device (REL_ATTN_EINVAL otherwise). The first split call on a
+ * device looks up the array's address there (hipGetSymbolAddress) and keeps
+ * it; make that first call outside graph capture.
+ */
+int rel_attn_fwd_noalloc(const void* q, const void* key_cache, const void* value_cache,
+                         const int32_t* block_table, const int32_t* cache_seqlens,
+                         const int32_t* cu_seqlens_q, const void* rel_logits, void* out, int dtype,
+                         int num_tokens, int batch_size, int max_seqlen_q, int max_blocks_per_seq,
+                         int num_heads, int num_kv_heads, int head_dim, int num_blocks,
+                         int block_size, int rel_extent, float softmax_scale, int causal,
+                         int window_left, int window_right, int num_splits, void* stream);
+
+/* rel_attn_noalloc_scratch_bytes - size in bytes of the static scratch array
+ * of rel_attn_fwd_noalloc (the largest split workspace it accepts). Host only. */
+size_t rel_attn_noalloc_scratch_bytes(void);
+
+/*
  * rel_attn_combine - merge the per-split partial results that
  * rel_attn_fwd_splits left in `workspace` (layout above) into `out`
  * [num_tokens][num_heads][head_dim] of type dtype:

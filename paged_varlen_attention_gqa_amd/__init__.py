@@ -12,7 +12,9 @@ from .relattn import (  # noqa: F401
     load_library,
     rel_attn_combine,
     rel_attn_fwd,
+    rel_attn_fwd_noalloc,
     rel_attn_fwd_splits,
+    rel_attn_noalloc_scratch_bytes,
     rel_attn_num_splits,
     rel_attn_strerror,
     rel_attn_workspace_bytes,

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/rel_attn.h"
 #include "kernels.h"
@@ -272,6 +273,81 @@ extern "C" int rel_attn_fwd_lse(const void* q, const void* key_cache, const void
 }
 
 #undef REL_ATTN_ARGS
+
+// ---- rel_attn_fwd_noalloc: the split-KV workspace in a static device array ----
+
+// The scratch memory of rel_attn_fwd_noalloc: room for the fp32 split-KV
+// workspace of calls that cannot allocate. Every GPU the library runs on
+// holds its own copy until the process ends. In host code this name stands
+// for no device address: kernels get the address hipGetSymbolAddress
+// returns for the current device (scratch_address below).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices];  // device address of `scratch`, per device
+
+// The device address of this GPU's scratch array. The stream must belong to
+// the current device; the address is looked up once per device, with that
+// device current, and kept.
+int scratch_address(hipStream_t stream, void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return REL_ATTN_ELAUNCH;
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return REL_ATTN_ELAUNCH;
+    if (sdev != dev) return REL_ATTN_EINVAL;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return REL_ATTN_ELAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return REL_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" size_t rel_attn_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+extern "C" int rel_attn_fwd_noalloc(const void* q, const void* key_cache, const void* value_cache,
+                                    const int32_t* block_table, const int32_t* cache_seqlens,
+                                    const int32_t* cu_seqlens_q, const void* rel_logits, void* out,
+                                    int dtype, int num_tokens, int batch_size, int max_seqlen_q,
+                                    int max_blocks_per_seq, int num_heads, int num_kv_heads,
+                                    int head_dim, int num_blocks, int block_size, int rel_extent,
+                                    float softmax_scale, int causal, int window_left, int window_right,
+                                    int num_splits, void* stream) {
+  // the size check and every argument check run before anything touches a
+  // device (the placeholder address only stands in for the scratch array in
+  // those checks and is never used)
+  const size_t need = rel_attn_workspace_bytes(num_splits, num_tokens, num_heads, head_dim);
+  if (num_splits > 1 && need > kScratchBytes) return REL_ATTN_EWORKSPACE;
+  void* workspace = nullptr;
+  {
+    AttnParams P;
+    bool launch = false;
+    void* const placeholder = reinterpret_cast<void*>(uintptr_t(256));
+    const int rc = prepare(q, key_cache, value_cache, block_table, cache_seqlens, cu_seqlens_q, rel_logits, out,
+                           dtype, num_tokens, batch_size, max_seqlen_q, max_blocks_per_seq, num_heads, num_kv_heads,
+                           head_dim, num_blocks, block_size, rel_extent, softmax_scale, causal, window_left,
+                           window_right, num_splits, placeholder, kScratchBytes, nullptr, &P, &launch);
+    if (rc != REL_ATTN_OK || !launch) return rc;
+  }
+  if (need > 0) {
+    const int rc = scratch_address(reinterpret_cast<hipStream_t>(stream), &workspace);
+    if (rc != REL_ATTN_OK) return rc;
+  }
+  return rel_attn_fwd(q, key_cache, value_cache, block_table, cache_seqlens, cu_seqlens_q, rel_logits, out, dtype,
+                      num_tokens, batch_size, max_seqlen_q, max_blocks_per_seq, num_heads, num_kv_heads, head_dim,
+                      num_blocks, block_size, rel_extent, softmax_scale, causal, window_left, window_right,
+                      num_splits, workspace, workspace ? kScratchBytes : 0, nullptr, stream);
+}
 
 extern "C" int rel_attn_combine(const void* workspace, size_t workspace_bytes, void* out, int dtype,
                                 int num_tokens, int num_heads, int head_dim, int num_splits,

@@ -61,6 +61,10 @@ def load_library() -> ctypes.CDLL:
     lib.rel_attn_fwd_lse.restype = c_int
     lib.rel_attn_combine.argtypes = [c_vp, c_size, c_vp] + [c_int] * 5 + [c_vp]
     lib.rel_attn_combine.restype = c_int
+    lib.rel_attn_fwd_noalloc.argtypes = lib.rel_attn_fwd.argtypes[:24] + [c_vp]  # no workspace arguments
+    lib.rel_attn_fwd_noalloc.restype = c_int
+    lib.rel_attn_noalloc_scratch_bytes.argtypes = []
+    lib.rel_attn_noalloc_scratch_bytes.restype = c_size
     _lib = lib
     return lib
 
@@ -146,6 +150,8 @@ def _attention_call(entry: str, q, key_cache, value_cache, *, block_table, cache
             if tuple(lse.shape) != (T, H):
                 raise ValueError(f"lse must be {(T, H)}, got {tuple(lse.shape)}")
     need = rel_attn_workspace_bytes(max(num_splits, 2) if with_lse else num_splits, T, H, D)
+    if entry == "rel_attn_fwd_noalloc":
+        need = 0  # the library's own scratch array holds the partials
     if need > 0:
         if workspace is None:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -153,6 +159,15 @@ def _attention_call(entry: str, q, key_cache, value_cache, *, block_table, cache
             _check_dev("workspace", workspace)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     stream = torch.cuda.current_stream(q.device).cuda_stream
+    if entry == "rel_attn_fwd_noalloc":
+        rc = lib.rel_attn_fwd_noalloc(
+            _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(block_table), _ptr(cache_seqlens),
+            _ptr(cu_seqlens_q), _ptr(rel_logits if rel_extent > 0 else None), _ptr(out),
+            dt, T, B, int(max_seqlen_q), block_table.shape[1], H, HKV, D, NB, BS, int(rel_extent),
+            float(softmax_scale), int(bool(causal)), wl, wr, int(num_splits), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RelAttnError(f"{entry}: {rel_attn_strerror(rc)} (code {rc})")
+        return out, None, num_splits
     lse_arg = [_ptr(lse)] if with_lse else []
     rc = getattr(lib, entry)(
         _ptr(q), _ptr(key_cache), _ptr(value_cache), _ptr(block_table), _ptr(cache_seqlens),
@@ -212,6 +227,29 @@ def rel_attn_fwd_splits(q: torch.Tensor, key_cache: torch.Tensor, value_cache: t
         softmax_scale=softmax_scale, causal=causal, window_size=window_size, rel_extent=rel_extent,
         rel_logits=rel_logits, num_splits=num_splits, out=out, workspace=workspace,
         max_kv_len=max_kv_len)
+
+
+def rel_attn_fwd_noalloc(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor, *,
+                         block_table: torch.Tensor, cache_seqlens: torch.Tensor,
+                         cu_seqlens_q: torch.Tensor, max_seqlen_q: int, softmax_scale: float,
+                         causal: bool, window_size=(-1, -1), rel_extent: int,
+                         rel_logits: torch.Tensor | None, num_splits: int | None = None,
+                         out: torch.Tensor | None = None, max_kv_len: int | None = None):
+    """:func:`rel_attn_fwd` through the entry point that allocates nothing: the
+    split partials go to the library's static scratch array (at most
+    :func:`rel_attn_noalloc_scratch_bytes` bytes). Pass ``out`` to keep the
+    call free of allocations on the Python side too."""
+    res, _, _ = _attention_call(
+        "rel_attn_fwd_noalloc", q, key_cache, value_cache, block_table=block_table,
+        cache_seqlens=cache_seqlens, cu_seqlens_q=cu_seqlens_q, max_seqlen_q=max_seqlen_q,
+        softmax_scale=softmax_scale, causal=causal, window_size=window_size, rel_extent=rel_extent,
+        rel_logits=rel_logits, num_splits=num_splits, out=out, workspace=None, max_kv_len=max_kv_len)
+    return res
+
+
+def rel_attn_noalloc_scratch_bytes() -> int:
+    """Size of the static scratch array behind :func:`rel_attn_fwd_noalloc`."""
+    return int(load_library().rel_attn_noalloc_scratch_bytes())
 
 
 def split_partials(workspace: torch.Tensor, num_splits: int, num_tokens: int, num_heads: int,

@@ -153,3 +153,39 @@ def test_combine_rejects_before_launch(lib, over, code):
 
 def test_combine_empty_call_is_ok(lib):
     assert _combine(lib, T=0, out=0) == 0
+
+
+def _noalloc(lib, **over):
+    a = dict(q=1, k=1, v=1, bt=1, sl=1, cu=1, rel=1, out=1, dtype=1, T=4, B=2, maxq=2, mb=3, H=8,
+             Hkv=2, D=128, NB=10, bs=16, E=4, scale=0.1, causal=1, wl=-1, wr=-1, splits=4, stream=None)
+    a.update(over)
+    ptr = lambda x: ctypes.c_void_p(x) if x else ctypes.c_void_p(0)  # noqa: E731
+    return lib.rel_attn_fwd_noalloc(
+        ptr(a["q"]), ptr(a["k"]), ptr(a["v"]), ptr(a["bt"]), ptr(a["sl"]), ptr(a["cu"]), ptr(a["rel"]),
+        ptr(a["out"]), a["dtype"], a["T"], a["B"], a["maxq"], a["mb"], a["H"], a["Hkv"], a["D"], a["NB"],
+        a["bs"], a["E"], a["scale"], a["causal"], a["wl"], a["wr"], a["splits"], ptr(a["stream"]))
+
+
+def test_noalloc_scratch_size(lib):
+    assert lib.rel_attn_noalloc_scratch_bytes() == 32 << 20
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(H=30, Hkv=4), -1),
+    (dict(splits=0), -1),
+    (dict(splits=513), -1),
+    (dict(q=0), -1),
+    (dict(rel=0), -1),
+    (dict(dtype=2), -2),
+    (dict(D=96), -2),
+    # a workspace of more than 32 MiB: 2 splits x 8192 tokens x 8 heads x 129 x 4 B
+    (dict(splits=2, T=8192), -3),
+    (dict(splits=512, T=64, H=32, Hkv=8), -3),
+])
+def test_noalloc_rejects_before_any_device_work(lib, over, code):
+    """Every check of rel_attn_fwd_noalloc runs on the host before a device is touched."""
+    assert _noalloc(lib, **over) == code
+
+
+def test_noalloc_empty_call_is_ok(lib):
+    assert _noalloc(lib, T=0, B=0, q=0, out=0) == 0
