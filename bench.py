@@ -4,9 +4,16 @@ A step is one attention call over one batch of synthetic, seeded input that
 is resident in HBM before timing starts: ``rel_attn_fwd_splits`` (the
 attention kernels) followed, when the call splits the key range, by
 ``rel_attn_combine`` -- together exactly what ``rel_attn_fwd`` launches.
-Default workload: batched decode, 64 requests x 1 query token, KV lengths
-uniform in [1024, 8192], 32 query / 8 KV heads, head_dim 128, block_size 16,
-rel_extent 1024, bf16.
+
+The metric has two halves, decode KV bandwidth and prefill TFLOP/s, and the
+default run times both, each for exactly ``--steps`` steps:
+  * the headline: batched decode, 64 requests x 1 query token, KV lengths
+    uniform in [1024, 8192], 32 query / 8 KV heads, head_dim 128, block_size
+    16, rel_extent 1024, bf16 (``value`` in GB/s);
+  * chunked causal prefill, 4 requests x 2048 queries over prior context
+    0/1024/2048/4096, 64 query / 8 KV heads, rel_extent 4096, bf16, reported
+    under ``config.prefill`` (TFLOP/s, with its own roofline and CPU baseline).
+``--config NAME`` times one workload alone.
 
 Prints ONE JSON line. ``value`` is the algorithmic bytes of a step (K/V rows
 of visible keys, in-range bias, q, out, page-table entries) divided by the
@@ -18,8 +25,9 @@ kernels run on, and compares that with MI355X's published peak. Its
 (FETCH_SIZE, WRITE_SIZE, scaled by the same counters' reading for a plain copy
 of known size), read from the committed counter summary under profiles/ when
 that summary was taken on the current kernel sources, else null.
-``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same
-workload.
+``cpu_baseline`` times the fp64 CPU oracle, unchanged, on a bounded sample of
+the same workload over the host's cores (at most 16), before the GPU is
+touched.
 """
 
 from __future__ import annotations
@@ -127,111 +135,110 @@ def _log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(case, name: str, budget_s: float = 20.0) -> dict:
-    """Time the fp64 oracle on a bounded sample of the same workload (whole requests
-    for decode workloads, a token sample otherwise); scaled to GB/s or TFLOP/s.
-    The oracle runs on one thread (its BLAS pool limited to 1), so ``cores`` is 1."""
+# ---- CPU baseline: the fp64 oracle on the host's cores ----
+# The pool is forked before this process touches the GPU, so that no worker
+# holds a device handle; workers inherit the case through _POOL_CASE.
+_POOL_CASE = None
+_POOL_LIMIT = None
+
+
+def _pool_init():
     from threadpoolctl import threadpool_limits
 
-    with threadpool_limits(limits=1):
-        return _cpu_baseline(case, name, budget_s)
+    global _POOL_LIMIT
+    _POOL_LIMIT = threadpool_limits(limits=1)  # one BLAS thread per worker
 
 
-def _cpu_baseline(case, name: str, budget_s: float) -> dict:
+def _pool_task(toks):
     import oracle
+
+    oracle.oracle_attention(**_POOL_CASE.kwargs(), tokens=toks)
+    return len(toks)
+
+
+def host_cores() -> int:
+    """Cores this process may use, capped at 16 (one GPU's share of a box)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(case, name: str, target_s: float = 10.0, budget_s: float = 20.0) -> dict:
+    """Time the fp64 oracle, unchanged, on a bounded sample of the same workload over the
+    host's cores (a forked pool, one BLAS thread per worker): whole requests for decode
+    workloads, the last 16 tokens of each request (in tasks of 2) for prefill workloads.
+    Passes over the sample repeat until about ``target_s`` of wall time (at most
+    ``budget_s``); the figure is the sample's algorithmic work over the wall time."""
+    import multiprocessing as mp
+
     from paged_varlen_attention_gqa_amd.work import count_work
 
+    global _POOL_CASE
     cu = case.cu_seqlens_q.tolist()
     B = case.batch_size
-    qlens, klens = case.query_lens(), case.kv_lens()
-    order = list(range(B))
-    done, t_total = [], 0.0
-    elem = case.q.element_size()
+    klens = case.kv_lens()
     bound = BOUND[name]
-    # passes over the requests until about 10 s of CPU time (a workload the
-    # oracle finishes sooner is repeated, for a steadier figure), at most budget_s
-    passes = 0
-    while t_total < min(10.0, budget_s):
-        passes += 1
-        for b in order:
-            toks = list(range(cu[b], cu[b + 1]))
-            if bound == "mfma":  # a bounded token sample of this request
-                toks = toks[-8:]
-            if not toks:
-                continue
+    tasks, task_req = [], []
+    for b in range(B):
+        toks = list(range(cu[b], cu[b + 1]))
+        if not toks:
+            continue
+        if bound == "mfma":
+            toks = toks[-16:]
+            for i in range(0, len(toks), 2):
+                tasks.append(toks[i:i + 2])
+                task_req.append(b)
+        else:
+            tasks.append(toks)
+            task_req.append(b)
+    cores = min(host_cores(), len(tasks))
+    _POOL_CASE = case
+    ctx = mp.get_context("fork")
+    done_q, done_k = [], []
+    wall, passes = 0.0, 0
+    with ctx.Pool(cores, initializer=_pool_init) as pool:
+        while wall < target_s and passes < 1000:
             t0 = time.perf_counter()
-            oracle.oracle_attention(**case.kwargs(), tokens=toks)
-            t_total += time.perf_counter() - t0
-            done.append((b, len(toks)))
-            if t_total > budget_s:
+            counts = pool.map(_pool_task, tasks, chunksize=1)
+            wall += time.perf_counter() - t0
+            passes += 1
+            for b, n in zip(task_req, counts):
+                done_q.append(n)
+                done_k.append(klens[b])
+            if wall > budget_s:
                 break
-        if t_total > budget_s or not done:
-            break
-    w = count_work(query_lens=[n for _, n in done], kv_lens=[klens[b] for b, _ in done],
-                   num_heads=case.num_heads, num_kv_heads=case.num_kv_heads, head_dim=case.head_dim,
-                   block_size=case.block_size, rel_extent=case.rel_extent, causal=case.causal,
-                   window_size=case.window_size, elem_bytes=elem)
-    cores = 1
+    _POOL_CASE = None
+    w = count_work(query_lens=done_q, kv_lens=done_k, num_heads=case.num_heads,
+                   num_kv_heads=case.num_kv_heads, head_dim=case.head_dim, block_size=case.block_size,
+                   rel_extent=case.rel_extent, causal=case.causal, window_size=case.window_size,
+                   elem_bytes=case.q.element_size())
     if bound == "mfma":
-        value, unit = w.flops / t_total / 1e12, "TFLOP/s"
+        value, unit = w.flops / wall / 1e12, "TFLOP/s"
+        what = f"the last 16 query tokens of each of the {B} requests"
     else:
-        value, unit = w.bytes / t_total / 1e9, "GB/s"
-    ntok = sum(n for _, n in done)
-    nreq = len(set(b for b, _ in done))
+        value, unit = w.bytes / wall / 1e9, "GB/s"
+        what = f"all {B} requests"
     return {"value": round(value, 6), "unit": unit, "cores": cores, "kind": "oracle",
-            "sample": f"{nreq} of {B} requests ({ntok} query tokens over {passes} pass(es), the last 8 of "
-                      f"each request for prefill), fp64 NumPy oracle, {t_total:.1f} s" if bound == "mfma" else
-                      f"{nreq} of {B} requests ({ntok} query tokens over {passes} pass(es)), fp64 NumPy "
-                      f"oracle, {t_total:.1f} s"}
+            "sample": f"{what} ({sum(done_q)} query tokens over {passes} pass(es)), fp64 NumPy oracle in a "
+                      f"pool of {cores} processes, {wall:.1f} s wall"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="decode_b64", choices=sorted(DESCRIPTIONS))
-    ap.add_argument("--num-splits", type=int, default=None)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold-steps", type=int, default=10,
-                    help="extra calls after the timed ones, each after a 1 GiB write that flushes the "
-                         "L2 and the 256 MB last-level cache (reported as stage_us_cold_mean)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="run a plain 2 GiB copy first (for HBM counter runs)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this path has no "
-              f"multi-GPU mode", file=sys.stderr)
-        sys.exit(2)
-    if not torch.cuda.is_available():
-        print("bench.py needs a ROCm GPU", file=sys.stderr)
-        sys.exit(2)
-    name = args.config
-    dev = torch.device("cuda:0")
-    _log(f"[bench] generating {name}")
-    case = make_case(**config_spec(name))
+# ---- GPU timing of one workload ----
+def time_workload(name: str, case, args, dev, splits_override=None) -> dict:
+    """Warm-up, then exactly ``args.steps`` timed steps; stage durations from HIP events on
+    the stream the kernels run on; then the same stage after cache flushes."""
     work = case_work(case)
     kw = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in case.kwargs().items()}
     wl, wr = case.window_size
-    splits = args.num_splits or rel_attn_num_splits(
+    splits = splits_override or rel_attn_num_splits(
         is_local=(wl >= 0 or wr >= 0), batch_size=case.batch_size, max_query_len=case.max_seqlen_q,
         num_heads=case.num_heads, num_kv_heads=case.num_kv_heads, max_kv_len=max(case.kv_lens()))
     out = torch.empty_like(kw["q"])
     need = rel_attn_workspace_bytes(splits, case.num_tokens, case.num_heads, case.head_dim)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-
-    if args.copy_calibration:
-        # a plain copy of known size, for scaling the HBM counters of a
-        # profiling run (2 GiB read + 2 GiB written, far beyond the caches)
-        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        _log(f"[bench] copy calibration: {COPY_BYTES} bytes read + written, 3 times")
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     def step(ev=None):
         if ev is not None:
@@ -242,13 +249,13 @@ def main():
         if splits > 1:
             rel_attn_combine(ws, out, splits)
 
-    _log(f"[bench] warmup {args.warmup} (num_splits={splits})")
+    _log(f"[bench] {name}: warmup {args.warmup} (num_splits={splits})")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
-    _log(f"[bench] timing {args.steps} steps")
+    _log(f"[bench] {name}: timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for ev in evs:
@@ -286,11 +293,9 @@ def main():
         roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
         value, unit = gbs, "GB/s"
-    res = {
-        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if case.dtype == torch.bfloat16 else "f32", "data": "synthetic",
+    del kw, out, ws
+    return {
+        "value": value, "unit": unit, "ms_per_step": ms_per_step, "roofline": roof,
         "config": {"workload": f"{name}: {DESCRIPTIONS[name]}", "num_splits": splits,
                    "algorithmic_bytes": work.bytes, "algorithmic_flops": work.flops,
                    "stage_kernels": STAGE_KERNELS[name],
@@ -298,11 +303,81 @@ def main():
                    "stage_us_min": round(float(stage_ms.min()) * 1e3, 2),
                    "stage_us_cold_mean": round(float(cold_ms.mean()) * 1e3, 2) if cold_ms.size else None,
                    "tflops": round(tflops, 3), "gbs": round(gbs, 2)},
-        "roofline": roof,
     }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=None, choices=sorted(DESCRIPTIONS),
+                    help="time this workload alone (default: decode_b64 as the headline, with "
+                         "prefill_chunked timed in the same run under config.prefill)")
+    ap.add_argument("--num-splits", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="extra calls after the timed ones, each after a 1 GiB write that flushes the "
+                         "L2 and the 256 MB last-level cache (reported as stage_us_cold_mean)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 2 GiB copy first (for HBM counter runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this path has no "
+              f"multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+    headline = args.config or "decode_b64"
+    names = [headline] if args.config else [headline, "prefill_chunked"]
+    cases = {}
+    for n in names:
+        _log(f"[bench] generating {n}")
+        cases[n] = make_case(**config_spec(n))
+    # the CPU baseline runs before this process touches the GPU (its pool is forked)
+    cpu = {}
     if not args.no_cpu_baseline:
-        _log("[bench] timing the CPU oracle on a bounded sample")
-        res["cpu_baseline"] = cpu_baseline(case, name)
+        for n in names:
+            _log(f"[bench] timing the CPU oracle on a bounded sample of {n}")
+            cpu[n] = cpu_baseline(cases[n], n)
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        # a plain copy of known size, for scaling the HBM counters of a
+        # profiling run (2 GiB read + 2 GiB written, far beyond the caches)
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        _log(f"[bench] copy calibration: {COPY_BYTES} bytes read + written, 3 times")
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    results = {}
+    for n in names:
+        results[n] = time_workload(n, cases[n], args, dev,
+                                   splits_override=args.num_splits if n == headline else None)
+        torch.cuda.empty_cache()
+    h = results[headline]
+    case = cases[headline]
+    res = {
+        "metric": METRIC, "value": round(h["value"], 3), "unit": h["unit"], "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(h["ms_per_step"], 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if case.dtype == torch.bfloat16 else "f32", "data": "synthetic",
+        "config": h["config"],
+        "roofline": h["roofline"],
+    }
+    for n in names[1:]:
+        r = results[n]
+        extra = dict(r["config"])
+        extra.update({"value": round(r["value"], 3), "unit": r["unit"], "steps": args.steps,
+                      "ms_per_step": round(r["ms_per_step"], 5), "roofline": r["roofline"]})
+        if n in cpu:
+            extra["cpu_baseline"] = cpu[n]
+        res["config"]["prefill" if n == "prefill_chunked" else n] = extra
+    if headline in cpu:
+        res["cpu_baseline"] = cpu[headline]
     print(json.dumps(res), flush=True)
 
 
