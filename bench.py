@@ -1,9 +1,8 @@
 """Benchmark: paged varlen GQA attention with the per-token relative bias on one MI355X.
 
-A step is one attention call over one batch of synthetic, seeded input that
-is resident in HBM before timing starts: ``rel_attn_fwd_splits`` (the
-attention kernels) followed, when the call splits the key range, by
-``rel_attn_combine`` -- together exactly what ``rel_attn_fwd`` launches.
+A step is one ``rel_attn_fwd`` call over one batch of synthetic, seeded
+input that is resident in HBM before timing starts: the attention kernels
+and, when the call splits the key range, the combine kernel.
 
 The metric has two halves, decode KV bandwidth and prefill TFLOP/s, and the
 default run times both, each for exactly ``--steps`` steps:
@@ -17,10 +16,13 @@ default run times both, each for exactly ``--steps`` steps:
 
 Prints ONE JSON line. ``value`` is the algorithmic bytes of a step (K/V rows
 of visible keys, in-range bias, q, out, page-table entries) divided by the
-wall-clock step time. ``roofline`` divides the same algorithmic figure (or
-the flops, for the compute-bound prefill workload) by the attention stage's
-own average duration, from HIP events recorded around it on the stream its
-kernels run on, and compares that with MI355X's published peak. Its
+wall-clock step time (the timed steps run back to back, with nothing
+recorded between them). ``roofline`` divides the same algorithmic figure (or
+the flops, for the compute-bound prefill workload) by the average duration
+of the attention kernels (``rel_attn_fwd_splits``; the combine kernel runs
+after the second event), from HIP events recorded around them in a second,
+untimed pass of as many steps, on the stream they run on, and compares that
+with MI355X's published peak. Its
 ``traffic`` is the HBM-side bytes per launch measured by rocprofv3 counters
 (FETCH_SIZE, WRITE_SIZE, scaled by the same counters' reading for a plain copy
 of known size), read from the committed counter summary under profiles/ when
@@ -46,8 +48,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-from paged_varlen_attention_gqa_amd import (rel_attn_combine, rel_attn_fwd_splits,  # noqa: E402
-                                           rel_attn_num_splits, rel_attn_workspace_bytes)
+from paged_varlen_attention_gqa_amd import (rel_attn_combine, rel_attn_fwd,  # noqa: E402
+                                           rel_attn_fwd_splits, rel_attn_num_splits,
+                                           rel_attn_workspace_bytes)
 from paged_varlen_attention_gqa_amd.inputs import config_spec, make_case  # noqa: E402
 from paged_varlen_attention_gqa_amd.work import case_work  # noqa: E402
 
@@ -92,10 +95,10 @@ STAGE_SOURCES = {
     "tiny_fp32": ["attn_general.hip"],
 }
 STAGE_KERNELS = {
-    "decode_b64": "attn_decode_balanced_kernel",
-    "decode_long_b1": "attn_decode_balanced_kernel",
-    "decode_1m_b1_kv4": "attn_decode_balanced_kernel",
-    "decode_1m_b1_kv8": "attn_decode_balanced_kernel",
+    "decode_b64": "attn_decode_balanced_kernel + combine_kernel",
+    "decode_long_b1": "attn_decode_balanced_kernel + combine_kernel",
+    "decode_1m_b1_kv4": "attn_decode_balanced_kernel + combine_kernel",
+    "decode_1m_b1_kv8": "attn_decode_balanced_kernel + combine_kernel",
     "prefill_chunked": "attn_decode_wg_split_kernel (no work: rows > 16) + attn_prefill_kernel",
     "mixed_window": "attn_decode_wg_split_kernel + attn_prefill_kernel",
     "tiny_fp32": "attn_general_kernel",
@@ -241,11 +244,13 @@ def time_workload(name: str, case, args, dev, splits_override=None) -> dict:
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+        if ev is None:
+            rel_attn_fwd(**kw, num_splits=splits, out=out, workspace=ws)
+            return
+        # the same launches, the attention kernels between the events
+        ev[0].record(stream)
         rel_attn_fwd_splits(**kw, num_splits=splits, out=out, workspace=ws)
-        if ev is not None:
-            ev[1].record(stream)
+        ev[1].record(stream)
         if splits > 1:
             rel_attn_combine(ws, out, splits)
 
@@ -253,17 +258,21 @@ def time_workload(name: str, case, args, dev, splits_override=None) -> dict:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    _log(f"[bench] {name}: timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    # the duration of each call, from events around it (a pass of its own, so
+    # that the event records do not sit between the timed steps)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
-    _log(f"[bench] {name}: timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for ev in evs:
         step(ev)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     stage_ms = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
-    ms_per_step = wall * 1e3 / args.steps
     # the same stage with no input left in the caches: a 1 GiB write before
     # each call (outside the events, not part of the timed steps)
     cold_ms = np.array([])
