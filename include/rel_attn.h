@@ -82,7 +82,9 @@ int rel_attn_num_splits(int is_local, int batch_size, int max_query_len, int num
 /*
  * rel_attn_workspace_bytes - size of the fp32 split-KV workspace that
  * rel_attn_fwd needs: num_splits * num_tokens * num_heads * (head_dim + 1) * 4
- * bytes when num_splits > 1, else 0. Returns 0 for invalid arguments.
+ * bytes when num_splits > 1, else 0. Returns 0 for invalid arguments, and
+ * SIZE_MAX when the size does not fit in size_t (no workspace is then
+ * accepted: the calls return REL_ATTN_EWORKSPACE).
  */
 size_t rel_attn_workspace_bytes(int num_splits, int num_tokens, int num_heads, int head_dim);
 

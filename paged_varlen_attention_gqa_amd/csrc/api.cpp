@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <initializer_list>
 #include <mutex>
 
 #include "../../include/rel_attn.h"
@@ -48,7 +49,7 @@ extern "C" int rel_attn_num_splits(int is_local, int batch_size, int max_query_l
     // request of the longest length then spans about (workgroups per group)
     // / batch pieces if all requests were that long; four times that leaves
     // room for shorter neighbours
-    const int64_t groups = (num_kv_heads + kDecodeHeadsPerWorkgroup - 1) / kDecodeHeadsPerWorkgroup;
+    const int64_t groups = ((int64_t)num_kv_heads + kDecodeHeadsPerWorkgroup - 1) / kDecodeHeadsPerWorkgroup;
     const int64_t per_group = kDecodeWorkgroups / groups > 0 ? kDecodeWorkgroups / groups : 1;
     int64_t splits = (4 * per_group + batch_size - 1) / batch_size + 2;
     const int64_t by_len = max_kv_len / kDecodeMinKeysPerPiece + 1;
@@ -60,8 +61,13 @@ extern "C" int rel_attn_num_splits(int is_local, int batch_size, int max_query_l
   // Prefill-shaped calls: split long key ranges until the launch has about
   // 4 workgroups per compute unit.
   const int64_t qtiles = (rows + kGeneralRows - 1) / kGeneralRows;
-  const int64_t units = (int64_t)batch_size * num_kv_heads * qtiles;
-  int64_t splits = (kTargetWorkgroups + units - 1) / units;
+  const int64_t pairs = (int64_t)batch_size * num_kv_heads;
+  // (the product of the two counts is taken only when it stays small)
+  int64_t splits = 1;
+  if (pairs < kTargetWorkgroups && qtiles < kTargetWorkgroups) {
+    const int64_t units = pairs * qtiles;
+    splits = (kTargetWorkgroups + units - 1) / units;
+  }
   const int64_t by_len = max_kv_len / kMinKeysPerSplit;
   if (splits > by_len) splits = by_len;
   if (splits > kMaxSplits) splits = kMaxSplits;
@@ -72,7 +78,14 @@ extern "C" int rel_attn_num_splits(int is_local, int batch_size, int max_query_l
 extern "C" size_t rel_attn_workspace_bytes(int num_splits, int num_tokens, int num_heads, int head_dim) {
   if (num_splits < 1 || num_tokens < 0 || num_heads < 1 || head_dim < 1) return 0;
   if (num_splits == 1) return 0;
-  return (size_t)num_splits * (size_t)num_tokens * (size_t)num_heads * (size_t)(head_dim + 1) * 4u;
+  // a size past what size_t holds is reported as SIZE_MAX, which no
+  // workspace can match (the call then fails with REL_ATTN_EWORKSPACE)
+  size_t n = (size_t)num_splits;
+  for (const size_t f : {(size_t)num_tokens, (size_t)num_heads, (size_t)head_dim + 1u, (size_t)4u}) {
+    if (f != 0 && n > SIZE_MAX / f) return SIZE_MAX;
+    n *= f;
+  }
+  return n;
 }
 
 extern "C" const char* rel_attn_strerror(int code) {
@@ -125,7 +138,7 @@ int prepare(const void* q, const void* key_cache, const void* value_cache, const
   if (rel_extent > 0 && num_tokens > 0 && rel_logits == nullptr) return REL_ATTN_EINVAL;
   if (batch_size > 65535 || num_kv_heads > 65535) return REL_ATTN_EUNSUPPORTED;
   if (num_splits > 1 && need > 0) {
-    if (workspace == nullptr || workspace_bytes < need) return REL_ATTN_EWORKSPACE;
+    if (workspace == nullptr || workspace_bytes < need || need == SIZE_MAX) return REL_ATTN_EWORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return REL_ATTN_EINVAL;
   }
   if (num_tokens == 0 || batch_size == 0 || max_seqlen_q == 0) return REL_ATTN_OK;
@@ -323,11 +336,11 @@ extern "C" int rel_attn_fwd_noalloc(const void* q, const void* key_cache, const 
                                     int head_dim, int num_blocks, int block_size, int rel_extent,
                                     float softmax_scale, int causal, int window_left, int window_right,
                                     int num_splits, void* stream) {
-  // the size check and every argument check run before anything touches a
-  // device (the placeholder address only stands in for the scratch array in
-  // those checks and is never used)
+  // every argument check, then the size check (a workspace of
+  // kScratchBytes), run before anything touches a device: the placeholder
+  // address only stands in for the scratch array in those checks and is
+  // never used
   const size_t need = rel_attn_workspace_bytes(num_splits, num_tokens, num_heads, head_dim);
-  if (num_splits > 1 && need > kScratchBytes) return REL_ATTN_EWORKSPACE;
   void* workspace = nullptr;
   {
     AttnParams P;
@@ -357,7 +370,7 @@ extern "C" int rel_attn_combine(const void* workspace, size_t workspace_bytes, v
   if (dtype != REL_ATTN_FP32 && dtype != REL_ATTN_BF16) return REL_ATTN_EUNSUPPORTED;
   if (!supported_head_dim(head_dim)) return REL_ATTN_EUNSUPPORTED;
   const size_t need = rel_attn_workspace_bytes(num_splits, num_tokens, num_heads, head_dim);
-  if (workspace == nullptr || workspace_bytes < need) return REL_ATTN_EWORKSPACE;
+  if (workspace == nullptr || workspace_bytes < need || need == SIZE_MAX) return REL_ATTN_EWORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return REL_ATTN_EINVAL;
   if (num_tokens == 0) return REL_ATTN_OK;
   if (out == nullptr) return REL_ATTN_EINVAL;
