@@ -319,7 +319,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default=None, choices=sorted(DESCRIPTIONS),
                     help="time this workload alone (default: decode_b64 as the headline, with "
                          "prefill_chunked timed in the same run under config.prefill)")

@@ -73,6 +73,10 @@ __device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t bytes) {
 // chunk swizzle of K/V LDS row r: a bijection of 0..15 that keeps 16
 // consecutive rows on distinct chunks and maps rows 4a..4a+3 to chunks that
 // differ in bits 1..3
+// a buffer offset past every resource's range (resources here span less
+// than 2 GB): such a copy returns zeros without a memory access
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
 __device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
 // global -> LDS copy of 1 KB per instruction: lane l writes bytes
@@ -391,12 +395,13 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
     }
   };
   // bias copies of the sub-tile at j0 into bias (the wave's slice); a
-  // sub-tile that no bias reaches (no_bias) re-reads the first entries of
-  // the resource (cached), so that it costs no HBM traffic
+  // sub-tile that no bias reaches (no_bias) reads at an offset past the
+  // resource's range, which returns zeros without touching memory, so that
+  // its slice holds zeros
   auto issue_bias = [&](char* my_bias, int j0, bool no_bias) {
-    const int hi = no_bias ? 0 : rel_last_byte;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) dma16(rel_rsrc, my_bias + 1024 * k, clamp0(cp_byte[k] - 2 * j0, hi));
+    for (int k = 0; k < 2; ++k)
+      dma16(rel_rsrc, my_bias + 1024 * k, no_bias ? kOutOfRange : clamp0(cp_byte[k] - 2 * j0, rel_last_byte));
   };
 
   f32x16_t oacc[kD / 32];  // O^T: dim tile mt, lane (h, n) reg a = dim 32mt + 8(a/4) + 4h + a%4
@@ -431,19 +436,17 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
     __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
   };
   // The start of the score accumulator of the sub-tile at j0: bias / scale,
-  // by two MFMAs (and, when the selection value is 1, an fp32 multiply)
-  // when the band reaches the sub-tile, else 0. Two rare cases first rewrite
+  // by two MFMAs (and, when the selection value is 1 and the band reaches
+  // the sub-tile, an fp32 multiply); outside the band the slice holds zeros
+  // and so does the result. Two rare cases first rewrite
   // the wave's slice in LDS (in branches that leave no values behind, so
   // that the common path reads the slice as it is): where the band covers
   // part of the tile, entries outside it are zeroed; in waves holding the
   // first or last row of rel_logits, pieces read at a clamped position are
   // shifted back into place.
   auto bias_acc = [&](char* my_bias, int j0, f32x16_t& s) {
-#pragma unroll
-    for (int a = 0; a < 16; ++a) s[a] = 0.f;
     const int bc = band_class(j0);
-    if (bc == 0) return;
-    if (bc == 2 || edge_wave) {
+    if (bc == 2 || (bc == 1 && edge_wave)) {
       asm volatile("");
       // piece u: entry x is distance e_lo0 - 16u + x (key 16u + 8h + 7 - x)
       const int e_lo0 = p - (j0 + 8 * h) - 7;
@@ -472,13 +475,16 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
     u32x4_t bb[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) bb[u] = *reinterpret_cast<const u32x4_t*>(my_bias + bias_rd[u]);
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, bias_sel[u]),
-                                                  __builtin_bit_cast(bf16x8v_t, bb[u]), s, 0, 0, 0);
+    const f32x16_t zero = {};
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, bias_sel[0]),
+                                                __builtin_bit_cast(bf16x8v_t, bb[0]), zero, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, bias_sel[1]),
+                                                __builtin_bit_cast(bf16x8v_t, bb[1]), s, 0, 0, 0);
     if constexpr (!kExactSel) {
+      if (bc != 0) {
 #pragma unroll
-      for (int a = 0; a < 16; ++a) s[a] *= inv_scale;
+        for (int a = 0; a < 16; ++a) s[a] *= inv_scale;
+      }
     }
   };
   // scores of keys a row does not see -> -inf (only on tiles some row does
