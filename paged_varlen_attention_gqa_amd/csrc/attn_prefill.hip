@@ -15,8 +15,8 @@
 //   * the relative bias is added by the matrix cores too: two more MFMAs per
 //     sub-tile multiply a constant one-hot selection matrix by the bias as
 //     the B operand, whose 8 k slots per lane are 8 consecutive entries of
-//     one rel_logits row (16-byte pieces of 64-byte runs per row, copied into
-//     aligned LDS slots). They start the sub-tile's score accumulator, and
+//     one rel_logits row (16-byte pieces of one 128-byte run per row and
+//     tile, copied into aligned LDS slots). They start the sub-tile's score accumulator, and
 //     the QK^T MFMAs accumulate on top. The selection value is
 //     1/softmax_scale when that is a bf16 number; otherwise it is 1 and the
 //     accumulator is multiplied by 1/softmax_scale in fp32 before the QK^T
@@ -52,8 +52,7 @@ constexpr int kRowBytes = kD * 2;
 constexpr int kSubBytes = kSub * kRowBytes;  // K (or V) rows of a sub-tile: 8 KB
 constexpr int kHalf = kKeys * kRowBytes;     // K (or V) part of a tile: 16 KB
 constexpr int kKV = 2 * kHalf;               // 32 KB
-constexpr int kBiasSub = 32 * kSub * 2;      // one wave's bias slice of a sub-tile: 2 KB
-constexpr int kBiasWave = 2 * kBiasSub;      // ... of a tile: 4 KB
+constexpr int kBiasWave = 32 * kKeys * 2;    // one wave's bias slice of a tile: 4 KB
 constexpr int kKvSlots = 2;                  // K/V ring: copies 1 tile ahead
 constexpr int kBiasSlots = 3;                // bias ring: copies 2 tiles ahead
 constexpr float kRescaleSlack = 8.0f;     // log2 units, as in the decode kernel
@@ -303,12 +302,17 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   const char* vbytes = reinterpret_cast<const char*>(P.v);
 
   // ---- relative-bias copy geometry ----
-  // The wave's slice of a tile is, for each of its 32 rows, the 32 entries
-  // d = p - j0 - 31 .. p - j0 (64 contiguous bytes) as four 16-byte pieces:
-  // piece q holds d = p - j0 - 31 + 8q .. +7, i.e. the bias of keys
-  // 16u + 8h + 7 - x for entry x with q = 3 - 2u - h. Copy instruction k
-  // moves rows 16k .. 16k + 15 whole (lane l: row 16k + l % 16, piece l / 16),
-  // so that it reads 16 runs of 64 bytes; its 1 KB lands in lane order.
+  // The wave's slice of a tile is, for each of its 32 rows, the 64 entries
+  // d = p - j0 - 63 .. p - j0 (128 contiguous bytes) as eight 16-byte
+  // pieces: piece q holds d = p - j0 - 63 + 8q .. +7. Pieces 4..7 serve the
+  // sub-tile at j0 and pieces 0..3 the one at j0 + 32; in sub-tile j, piece
+  // (3 - 2u - h) + 4(1 - j) holds the bias of keys 16u + 8h + 7 - x for entry
+  // x. Copy instruction m moves rows 8m .. 8m + 7 whole: lane l takes row
+  // r = 8m + l / 8 and lands in its LDS row at slot l % 8, which holds piece
+  // (l % 8) ^ ((r / 2) % 8) (the slots of a row are XOR-swizzled so that
+  // each 16-lane group of a piece read covers all banks once). One
+  // instruction thus reads 8 runs of 128 bytes; its 1 KB lands in lane
+  // order.
   // Copies read through one resource over the wave's rows plus 64 entries
   // on each side (inside the tensor). A piece is read from its position
   // clamped into the resource: with E >= 8 a piece moved that way holds an
@@ -334,20 +338,27 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   const int rel_lane_elem = (int)(my_row_abs * E - reg_lo);  // row start, relative to the resource
   const int rel_last_piece = (int)(reg_hi - reg_lo) - 8;      // last piece start inside the resource
   const int rel_last_byte = 2 * rel_last_piece;
-  // the rows this lane copies (k = 0, 1): byte offset of the first entry of
-  // piece 0 of the tile at key 0, relative to the resource
-  int cp_byte[2];
+  // the pieces this lane copies (m = 0..3): byte offset of the piece's first
+  // entry for the tile at key 0, relative to the resource; cp_second: the
+  // piece serves the second sub-tile
+  int cp_byte[4];
+  bool cp_second[4];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int rc = min(r0 + 32 * wave + 16 * k + (lane & 15), nrows - 1);
+  for (int m = 0; m < 4; ++m) {
+    const int piece = (lane & 7) ^ ((4 * (m & 1) + (lane >> 4)) & 7);
+    cp_second[m] = piece < 4;
+    const int rc = min(r0 + 32 * wave + 8 * m + (lane >> 3), nrows - 1);
     const int itok_c = rc / G;
     const int64_t row_abs_c = (int64_t)(t0 + itok_c) * P.H + g * G + rc % G;
-    cp_byte[k] = 2 * ((int)(row_abs_c * E - reg_lo) + (itok_c + L - S) - 31 + 8 * (lane >> 4));
+    cp_byte[m] = 2 * ((int)(row_abs_c * E - reg_lo) + (itok_c + L - S) - 63 + 8 * piece);
   }
-  // where lane (h, n) finds its piece u of its row
-  uint32_t bias_rd[2];
+  // where lane (h, n) finds piece u of sub-tile j of its row
+  uint32_t bias_rd[2][2];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) bias_rd[u] = (uint32_t)(1024 * (n >> 4) + 16 * ((n & 15) + 16 * (3 - 2 * u - h)));
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      bias_rd[j][u] = (uint32_t)(1024 * (n >> 3) + 128 * (n & 7) + 16 * (((3 - 2 * u - h) + 4 * (1 - j)) ^ ((n >> 1) & 7)));
   const bool edge_row = E > 0 && row_ok && (my_row_abs == 0 || my_row_abs == (int64_t)P.T * P.H - 1);
   // distances covered by a sub-tile over the workgroup's rows: [p_lo - j0 - 31, p_hi - j0]
   const int p_lo = ia + L - S, p_hi = ib + L - S;
@@ -394,14 +405,16 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
       dma16_soff(v_rsrc, kv + kSubBytes * j + v_dst, v_src, off);
     }
   };
-  // bias copies of the sub-tile at j0 into bias (the wave's slice); a
-  // sub-tile that no bias reaches (no_bias) reads at an offset past the
-  // resource's range, which returns zeros without touching memory, so that
-  // its slice holds zeros
-  auto issue_bias = [&](char* my_bias, int j0, bool no_bias) {
+  // bias copies of the tile at j0 into bias (the wave's slice); the pieces
+  // of a sub-tile that no bias reaches read at an offset past the resource's
+  // range, which returns zeros without touching memory, so that they hold
+  // zeros
+  auto issue_bias = [&](char* my_bias, int j0) {
+    const bool none0 = band_class(j0) == 0, none1 = band_class(j0 + kSub) == 0;
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
-      dma16(rel_rsrc, my_bias + 1024 * k, no_bias ? kOutOfRange : clamp0(cp_byte[k] - 2 * j0, rel_last_byte));
+    for (int m = 0; m < 4; ++m)
+      dma16(rel_rsrc, my_bias + 1024 * m,
+            (cp_second[m] ? none1 : none0) ? kOutOfRange : clamp0(cp_byte[m] - 2 * j0, rel_last_byte));
   };
 
   f32x16_t oacc[kD / 32];  // O^T: dim tile mt, lane (h, n) reg a = dim 32mt + 8(a/4) + 4h + a%4
@@ -444,7 +457,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   // part of the tile, entries outside it are zeroed; in waves holding the
   // first or last row of rel_logits, pieces read at a clamped position are
   // shifted back into place.
-  auto bias_acc = [&](char* my_bias, int j0, f32x16_t& s) {
+  auto bias_acc = [&](char* my_bias, int j, int j0, f32x16_t& s) {
     const int bc = band_class(j0);
     if (bc == 2 || (bc == 1 && edge_wave)) {
       asm volatile("");
@@ -452,7 +465,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
       const int e_lo0 = p - (j0 + 8 * h) - 7;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        u32x4_t v = *reinterpret_cast<const u32x4_t*>(my_bias + bias_rd[u]);
+        u32x4_t v = *reinterpret_cast<const u32x4_t*>(my_bias + bias_rd[j][u]);
         if (edge_wave) {
           // a piece read at `at` instead of `want` has its entries moved
           // back by want - at
@@ -467,14 +480,14 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
           const uint32_t hi_ok = (uint32_t)(e + 1) < (uint32_t)E ? 0xffff0000u : 0u;
           v[w] &= lo_ok | hi_ok;
         }
-        *reinterpret_cast<u32x4_t*>(my_bias + bias_rd[u]) = v;
+        *reinterpret_cast<u32x4_t*>(my_bias + bias_rd[j][u]) = v;
       }
       // the common path below reloads the slice
       asm volatile("" ::: "memory");
     }
     u32x4_t bb[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) bb[u] = *reinterpret_cast<const u32x4_t*>(my_bias + bias_rd[u]);
+    for (int u = 0; u < 2; ++u) bb[u] = *reinterpret_cast<const u32x4_t*>(my_bias + bias_rd[j][u]);
     const f32x16_t zero = {};
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, bias_sel[0]),
                                                 __builtin_bit_cast(bf16x8v_t, bb[0]), zero, 0, 0, 0);
@@ -558,10 +571,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
     auto j0_of = [&](int it) { return kstart + kKeys * min(it, last); };
     auto kv_slot = [&](int i) { return kv_buf + i * kKV; };
     auto b_slot = [&](int i) { return bias_buf + i * (kWaves * kBiasWave) + wave * kBiasWave; };
-    auto issue_bias_tile = [&](int slot, int j0) {
-      issue_bias(b_slot(slot), j0, band_class(j0) == 0);
-      issue_bias(b_slot(slot) + kBiasSub, j0 + kSub, band_class(j0 + kSub) == 0);
-    };
+    auto issue_bias_tile = [&](int slot, int j0) { issue_bias(b_slot(slot), j0); };
     // copies of the stages before tb: bias tb, K/V tb, bias tb + 1
     issue_bias_tile(0, j0_of(tb));
     issue_kv(kv_slot(0), 0, j0_of(tb), page_of(j0_of(tb)));
@@ -593,7 +603,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
       // S^T = bias / scale + K Q^T of the two sub-tiles
       f32x16_t sc[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bias_acc(b_slot(b_i) + kBiasSub * j, j0 + kSub * j, sc[j]);
+      for (int j = 0; j < 2; ++j) bias_acc(b_slot(b_i), j, j0 + kSub * j, sc[j]);
       qk2(kv, sc);
       mask_scores(j0, sc);
       // row max of the unscaled scores, scaled (log2 units); a new reference
