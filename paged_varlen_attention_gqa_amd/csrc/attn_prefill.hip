@@ -170,12 +170,18 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   char* const kv_buf = lds;
   char* const bias_buf = lds + kKvSlots * kKV;
 
-  const int b = blockIdx.z;
-  const int g = blockIdx.y;
+  // Dispatch order (the linear workgroup id): KV head fastest, then query
+  // tile (longest causal key range first), then request. Workgroups go to
+  // the 8 XCDs in turn, so that with 8 KV heads each XCD works through one
+  // head of one request at a time and its L2 serves that K/V stream to all
+  // of them (measured: faster than tile-fastest or request-fastest orders).
+  const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int g = lin % gridDim.y;
+  const int bx = (lin / gridDim.y) % gridDim.x;
+  const int b = lin / (gridDim.y * gridDim.x);
   const int qtiles = gridDim.x / P.splits;
-  // longest query tiles (largest causal key range) first
-  const int qt = qtiles - 1 - (int)(blockIdx.x / P.splits);
-  const int split = blockIdx.x % P.splits;
+  const int qt = qtiles - 1 - bx / P.splits;
+  const int split = bx % P.splits;
   int t0, S, L;
   if (!request_bounds(P, b, t0, S, L)) return;
   const int G = P.G;
