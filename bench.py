@@ -168,6 +168,18 @@ def host_cores() -> int:
     return max(1, min(16, n))
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown CPU"."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def cpu_baseline(case, name: str, target_s: float = 10.0, budget_s: float = 20.0) -> dict:
     """Time the fp64 oracle, unchanged, on a bounded sample of the same workload over the
     host's cores (a forked pool, one BLAS thread per worker): whole requests for decode
@@ -225,7 +237,7 @@ def cpu_baseline(case, name: str, target_s: float = 10.0, budget_s: float = 20.0
         what = f"all {B} requests"
     return {"value": round(value, 6), "unit": unit, "cores": cores, "kind": "oracle",
             "sample": f"{what} ({sum(done_q)} query tokens over {passes} pass(es)), fp64 NumPy oracle in a "
-                      f"pool of {cores} processes, {wall:.1f} s wall"}
+                      f"pool of {cores} processes on {cpu_model()}, {wall:.1f} s wall"}
 
 
 # ---- GPU timing of one workload ----
