@@ -415,10 +415,11 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   // of a sub-tile that no bias reaches read at an offset past the resource's
   // range, which returns zeros without touching memory, so that they hold
   // zeros
-  auto issue_bias = [&](char* my_bias, int j0) {
+  // (copy instructions m_lo .. m_hi - 1 of the four)
+  auto issue_bias = [&](char* my_bias, int j0, int m_lo = 0, int m_hi = 4) {
     const bool none0 = band_class(j0) == 0, none1 = band_class(j0 + kSub) == 0;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = m_lo; m < m_hi; ++m)
       dma16(rel_rsrc, my_bias + 1024 * m,
             (cp_second[m] ? none1 : none0) ? kOutOfRange : clamp0(cp_byte[m] - 2 * j0, rel_last_byte));
   };
@@ -598,19 +599,23 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
       const int j0 = j0_of(s);
       const int jn = j0_of(s + 1);
       const int j2 = j0_of(s + 2);
-      issue_kv(kv_slot(kv_i ^ 1), 0, jn, page0);
-      issue_kv(kv_slot(kv_i ^ 1), 1, jn, page1);
       constexpr int b_n = b_i == 0 ? 2 : b_i - 1;  // slot of tile s - 1 = slot of tile s + 2
-      issue_bias_tile(b_n, j2);
       page_next0 = page_of(j2);
       page_next1 = page_of(j2 + kSub);
       char* kv = kv_slot(kv_i);
       if (j0 + kKeys > L) zero_v_tail(kv, j0);
-      // S^T = bias / scale + K Q^T of the two sub-tiles
+      // S^T = bias / scale + K Q^T of the two sub-tiles. The copies of later
+      // tiles (K/V of tile s + 1, then the bias of tile s + 2, in that order
+      // as the waits assume) are spread over the stage instead of leaving
+      // together after the barrier, so that the vector memory path takes
+      // them while the stage computes (measured: 3% faster)
       f32x16_t sc[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) bias_acc(b_slot(b_i), j, j0 + kSub * j, sc[j]);
+      bias_acc(b_slot(b_i), 0, j0, sc[0]);
+      issue_kv(kv_slot(kv_i ^ 1), 0, jn, page0);
+      bias_acc(b_slot(b_i), 1, j0 + kSub, sc[1]);
+      issue_kv(kv_slot(kv_i ^ 1), 1, jn, page1);
       qk2(kv, sc);
+      issue_bias(b_slot(b_n), j2, 0, 2);
       mask_scores(j0, sc);
       // row max of the unscaled scores, scaled (log2 units); a new reference
       // only when it grows by more than the slack
@@ -645,6 +650,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
           for (int w = 0; w < 4; ++w) l_part = dot2_bf16_ones(pb[kb][w], l_part);
         }
         pv(kv, j, pb);
+        if (j == 0) issue_bias(b_slot(b_n), j2, 2, 4);
       }
     };
     using I0 = std::integral_constant<int, 0>;
