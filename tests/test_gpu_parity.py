@@ -63,6 +63,15 @@ def test_full_decode_1m_b1(name):
     _check(make_config(name))
 
 
+def _run_of_tokens(rng, S, n):
+    """n consecutive query tokens of a request with S tokens, starting at a
+    random multiple of n: with G query heads per KV head they are n * G
+    consecutive packed rows, so every row position of a block of that many
+    rows is compared."""
+    start = n * int(rng.integers(0, S // n))
+    return range(start, start + n)
+
+
 def test_full_prefill_chunked_sampled():
     case = make_config("prefill_chunked")
     cu = case.cu_seqlens_q.tolist()
@@ -70,8 +79,8 @@ def test_full_prefill_chunked_sampled():
     tokens = set()
     for b in range(case.batch_size):
         S = cu[b + 1] - cu[b]
-        for i in list(rng.choice(S, 6, replace=False)) + [0, S - 1]:
-            tokens.add(cu[b] + int(i))
+        picks = list(rng.choice(S, 12, replace=False)) + [0, S - 1] + list(_run_of_tokens(rng, S, 32))
+        tokens.update(cu[b] + int(i) for i in picks)
     _check(case, tokens=tokens, what="prefill_chunked sampled")
 
 
@@ -82,8 +91,10 @@ def test_full_mixed_window_sampled():
     tokens = set(range(cu[8], cu[-1]))  # every decode token
     for b in range(8):
         S = cu[b + 1] - cu[b]
-        for i in list(rng.choice(S, 3, replace=False)) + [0, S - 1]:
-            tokens.add(cu[b] + int(i))
+        picks = list(rng.choice(S, 3, replace=False)) + [0, S - 1]
+        if b % 2 == 0:
+            picks += list(_run_of_tokens(rng, S, 32))
+        tokens.update(cu[b] + int(i) for i in picks)
     _check(case, tokens=tokens, what="mixed_window sampled")
 
 
