@@ -368,11 +368,16 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   const bool edge_row = E > 0 && row_ok && (my_row_abs == 0 || my_row_abs == (int64_t)P.T * P.H - 1);
   // distances covered by a sub-tile over the workgroup's rows: [p_lo - j0 - 31, p_hi - j0]
   const int p_lo = ia + L - S, p_hi = ib + L - S;
-  // sub-tile at j0 -> 0: no key gets a bias, 1: every score does, 2: some do
+  // sub-tile at j0 -> 0: no key gets a bias, 1: every score does, 2: some
+  // do; as thresholds on j0: none when j0 <= band_a (every distance >= E) or
+  // j0 > band_d (every distance < 0), all when band_b < j0 <= band_c
+  const int band_a = E == 0 ? 0x7fffffff : p_lo - (kSub - 1) - E;
+  const int band_b = p_hi - E, band_c = p_lo - (kSub - 1), band_d = p_hi;
   auto band_class = [&](int j0) -> int {
-    if (E == 0 || p_hi - j0 < 0 || p_lo - (j0 + kSub - 1) >= E) return 0;
-    if (p_lo - (j0 + kSub - 1) >= 0 && p_hi - j0 < E) return 1;
-    return 2;
+    const int js = __builtin_amdgcn_readfirstlane(j0);
+    const bool none = (js <= band_a) | (js > band_d);
+    const bool all = (js > band_b) & (js <= band_c);
+    return none ? 0 : (all ? 1 : 2);
   };
   // A operand of the bias MFMAs: lane (h', m) holds row m (key sigma(m)) and
   // k slots 8h' + x; slot x of part u stands for key 16u + 8h' + 7 - x; the
@@ -415,13 +420,22 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   // of a sub-tile that no bias reaches read at an offset past the resource's
   // range, which returns zeros without touching memory, so that they hold
   // zeros
-  // (copy instructions m_lo .. m_hi - 1 of the four)
-  auto issue_bias = [&](char* my_bias, int j0, int m_lo = 0, int m_hi = 4) {
-    const bool none0 = band_class(j0) == 0, none1 = band_class(j0 + kSub) == 0;
+  // (copy instructions m_lo .. m_hi - 1 of the four; none0 / none1: the
+  // first / second sub-tile is outside the band)
+  auto issue_bias_nn = [&](char* my_bias, int j0, bool none0, bool none1, int m_lo, int m_hi) {
+    if (!(none0 | none1)) {
+      // both sub-tiles reach the band (the common case)
 #pragma unroll
-    for (int m = m_lo; m < m_hi; ++m)
-      dma16(rel_rsrc, my_bias + 1024 * m,
-            (cp_second[m] ? none1 : none0) ? kOutOfRange : clamp0(cp_byte[m] - 2 * j0, rel_last_byte));
+      for (int m = m_lo; m < m_hi; ++m) dma16(rel_rsrc, my_bias + 1024 * m, clamp0(cp_byte[m] - 2 * j0, rel_last_byte));
+    } else {
+#pragma unroll
+      for (int m = m_lo; m < m_hi; ++m)
+        dma16(rel_rsrc, my_bias + 1024 * m,
+              (cp_second[m] ? none1 : none0) ? kOutOfRange : clamp0(cp_byte[m] - 2 * j0, rel_last_byte));
+    }
+  };
+  auto issue_bias = [&](char* my_bias, int j0, int m_lo = 0, int m_hi = 4) {
+    issue_bias_nn(my_bias, j0, band_class(j0) == 0, band_class(j0 + kSub) == 0, m_lo, m_hi);
   };
 
   f32x16_t oacc[kD / 32];  // O^T: dim tile mt, lane (h, n) reg a = dim 32mt + 8(a/4) + 4h + a%4
@@ -438,22 +452,25 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   // (h, n) is key j0 + 16h + a; the two MFMA chains interleaved (a chain's
   // next step waits for its previous one)
   auto qk2 = [&](const char* kv, f32x16_t* s) {
+    // K operand reads run two steps ahead of the matrix instructions (order
+    // pinned with scheduling barriers)
+    u32x4_t kf[3][2];
+    auto load = [&](int kk) {
 #pragma unroll
-    for (int kk = 0; kk < kD / 16; ++kk)
+      for (int j = 0; j < 2; ++j) kf[kk % 3][j] = *reinterpret_cast<const u32x4_t*>(kv + kSubBytes * j + k_rd[kk]);
+    };
+    load(0);
+    load(1);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kv + kSubBytes * j + k_rd[kk]);
-        s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, kf),
+    for (int kk = 0; kk < kD / 16; ++kk) {
+      if (kk + 2 < kD / 16) load(kk + 2);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v_t, kf[kk % 3][j]),
                                                        __builtin_bit_cast(bf16x8v_t, qreg[kk]), s[j], 0, 0, 0);
-      }
-    // K operand reads run three steps ahead of the matrix instructions
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-    for (int i = 0; i < 5; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
   };
   // The start of the score accumulator of the sub-tile at j0: bias / scale,
   // by two MFMAs (and, when the selection value is 1 and the band reaches
@@ -464,8 +481,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   // part of the tile, entries outside it are zeroed; in waves holding the
   // first or last row of rel_logits, pieces read at a clamped position are
   // shifted back into place.
-  auto bias_acc = [&](char* my_bias, int j, int j0, f32x16_t& s) {
-    const int bc = band_class(j0);
+  auto bias_acc = [&](char* my_bias, int j, int j0, int bc, f32x16_t& s) {
     if (bc == 2 || (bc == 1 && edge_wave)) {
       asm volatile("");
       // piece u: entry x is distance e_lo0 - 16u + x (key 16u + 8h + 7 - x)
@@ -608,14 +624,17 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
       // tiles (K/V of tile s + 1, then the bias of tile s + 2, in that order
       // as the waits assume) are spread over the stage instead of leaving
       // together after the barrier, so that the vector memory path takes
-      // them while the stage computes (measured: 3% faster)
+      // them while the stage computes (measured: 3% faster). The band classes
+      // of the sub-tiles computed and copied are taken once per stage.
+      const int bc0 = band_class(j0), bc1 = band_class(j0 + kSub);
+      const bool nn0 = band_class(j2) == 0, nn1 = band_class(j2 + kSub) == 0;
       f32x16_t sc[2];
-      bias_acc(b_slot(b_i), 0, j0, sc[0]);
+      bias_acc(b_slot(b_i), 0, j0, bc0, sc[0]);
       issue_kv(kv_slot(kv_i ^ 1), 0, jn, page0);
-      bias_acc(b_slot(b_i), 1, j0 + kSub, sc[1]);
+      bias_acc(b_slot(b_i), 1, j0 + kSub, bc1, sc[1]);
       issue_kv(kv_slot(kv_i ^ 1), 1, jn, page1);
       qk2(kv, sc);
-      issue_bias(b_slot(b_n), j2, 0, 2);
+      issue_bias_nn(b_slot(b_n), j2, nn0, nn1, 0, 2);
       mask_scores(j0, sc);
       // row max of the unscaled scores, scaled (log2 units); a new reference
       // only when it grows by more than the slack
@@ -650,7 +669,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
           for (int w = 0; w < 4; ++w) l_part = dot2_bf16_ones(pb[kb][w], l_part);
         }
         pv(kv, j, pb);
-        if (j == 0) issue_bias(b_slot(b_n), j2, 2, 4);
+        if (j == 0) issue_bias_nn(b_slot(b_n), j2, nn0, nn1, 2, 4);
       }
     };
     using I0 = std::integral_constant<int, 0>;
