@@ -69,14 +69,16 @@ __device__ __forceinline__ u32x4_t make_rsrc(const void* base, uint32_t bytes) {
 }
 
 
-// chunk swizzle of K/V LDS row r: a bijection of 0..15 that keeps 16
-// consecutive rows on distinct chunks and maps rows 4a..4a+3 to chunks that
-// differ in bits 1..3
 // a buffer offset past every resource's range (resources here span less
 // than 2 GB): such a copy returns zeros without a memory access
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
+// chunk swizzle of K LDS row r: a bijection of 0..15, so that the 16 rows
+// of a K operand read (16 lanes of 16 bytes each) fall on distinct chunks
 __device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// chunk swizzle of V LDS row r: 4 (r % 4), so that the four consecutive rows
+// of a transpose read land on different chunk groups
+__device__ __forceinline__ int swz_v(int r) { return (r & 3) << 2; }
 
 // global -> LDS copy of 1 KB per instruction: lane l writes bytes
 // [16l, 16l+16) of the LDS block at lds. Issued from inline assembly so that
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
     const int krow = krow0 + (lane >> 4);
     const int vrow = key + (lane >> 4);
     k_src = (uint32_t)(lane >> 4) * row_bytes + 16u * (uint32_t)((lane & 15) ^ swz(krow));
-    v_src = (uint32_t)(lane >> 4) * row_bytes + 16u * (uint32_t)((lane & 15) ^ swz(vrow));
+    v_src = (uint32_t)(lane >> 4) * row_bytes + 16u * (uint32_t)((lane & 15) ^ swz_v(vrow));
     k_dst = krow0 * kRowBytes;          // + kSubBytes * sub-tile
     v_dst = kHalf + key * kRowBytes;    // + kSubBytes * sub-tile
   }
@@ -263,20 +265,21 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
   for (int kk = 0; kk < kD / 16; ++kk)
     k_rd[kk] = (uint32_t)(n * kRowBytes + 16 * ((2 * kk) ^ (h ^ swz(n & 15))));
   // transpose reads of V for (block kb, dim tile mt, group sr): lane
-  // (h, n), j = n%16, points at row 16h + 8kb + 4sr + j/4 and element
-  // 32mt + 16(n/16) + 4(j%4). The row's swizzle is 8sr + 2(j/4) + kb, so the
-  // chunk is Y ^ (4mt ^ 8sr ^ kb) with Y = 2(n/16) + (j%4)/2 ^ 2(j/4): one
-  // lane value XOR a constant of (mt, sr, kb).
-  uint32_t v_rd[8];  // index: kb | (mt&1)<<1 | ((mt>>1)^sr)<<2
+  // (h, n), j = n%16, points at row 16h + 8kb + 4sr + j/4, logical chunk
+  // 4mt + 2(n/16) + (j%4)/2 (elements 32mt + 16(n/16) + 4(j%4) ..), half
+  // j%2. The 32 lanes of a read cover 4 rows x 64 bytes; with the V swizzle
+  // 4 (row % 4) the four rows fall on different chunk groups, so the read
+  // touches every bank twice (no conflicts), and the chunk is
+  // (4mt + 2(n/16) + (j%4)/2) ^ 4(j/4): one register per mt, the block and
+  // group enter as row offsets.
+  uint32_t v_rd[4];
   {
     const int j = n & 15;
-    const int Y = (2 * (n >> 4) + ((j & 3) >> 1)) ^ (2 * (j >> 2));
-    const uint32_t base = (uint32_t)((16 * h + (j >> 2)) * kRowBytes + 8 * (j & 1));
+    const int q = j >> 2;
+    const uint32_t base = (uint32_t)((16 * h + q) * kRowBytes + 8 * (j & 1));
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int C = (c & 1) | ((c >> 1) & 1) << 2 | ((c >> 2) & 1) << 3;
-      v_rd[c] = base + 16u * (uint32_t)(Y ^ C);
-    }
+    for (int mt = 0; mt < 4; ++mt)
+      v_rd[mt] = base + 16u * (uint32_t)((4 * mt + 2 * (n >> 4) + ((j & 3) >> 1)) ^ (4 * q));
   }
 
   const int bs_log2 = P.bs_log2;
@@ -549,8 +552,7 @@ __global__ __launch_bounds__(kWaves * 64) void attn_prefill_kernel(AttnParams P,
         u32x2_t part[2];
 #pragma unroll
         for (int sr = 0; sr < 2; ++sr) {
-          const int c = kb | ((mt & 1) << 1) | ((((mt >> 1) ^ sr) & 1) << 2);
-          const char* addr = kv + kHalf + kSubBytes * j + (8 * kb + 4 * sr) * kRowBytes + v_rd[c];
+          const char* addr = kv + kHalf + kSubBytes * j + (8 * kb + 4 * sr) * kRowBytes + v_rd[mt];
           part[sr] = __builtin_bit_cast(
               u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)addr));
         }
