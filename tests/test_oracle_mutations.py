@@ -59,6 +59,12 @@ MUTATIONS = [
     ("lse_empty_zero", "np.where(has, m + np.log(np.where(has, l, 1.0)), NEG_INF)",
      "np.where(has, m + np.log(np.where(has, l, 1.0)), 0.0)"),
     ("lse_sum_without_max", "l = w.sum(axis=1)", "l = w.sum(axis=1) * np.exp(m)"),
+    ("window_left_zero_ignored", "    if wl >= 0:\n        lo = max(lo, p - wl)",
+     "    if wl > 0:\n        lo = max(lo, p - wl)"),
+    ("empty_row_nan", "o = np.zeros((len(rows), D))", "o = np.full((len(rows), D), np.nan)"),
+    ("pages_of_first_request", "pages = block_table[b, :npages]", "pages = block_table[0, :npages]"),
+    ("query_rows_no_offset", "qh = _f64(q[t0 + rows, h, :])", "qh = _f64(q[rows, h, :])"),
+    ("output_rows_no_offset", "out[t0 + rows, h, :] = o", "out[rows, h, :] = o"),
 ]
 
 
